@@ -1,0 +1,173 @@
+"""CPU oracle of one Beam mixture-of-experts layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the GPU library and never calls it.
+
+The arithmetic lives in ``beam_oracle.c`` (plain loops, fp64; the routing choice is taken
+on fp32 values as the Beam model doc's FP32-numerics paragraph fixes).  This wrapper only
+marshals numpy arrays.  Each function cites the passage it follows in the C file.
+
+Pins: every function here is checked against closed forms, invariants, brute force and
+hand-worked cases in ``tests/test_oracle_pins.py`` (see that file's docstring).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "beam_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# a planted-mistake copy of the oracle can be loaded instead (tests/test_oracle_mutations.py)
+_LIB_OVERRIDE = os.environ.get("BEAM_ORACLE_LIB")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (portable x86-64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-o", tmp, _SRC,
+                               "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB)
+        vp, i64, i32, f32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+        lib.oracle_rmsnorm_pinned.argtypes = [vp, vp, f32, i64, i64, vp]
+        lib.oracle_rmsnorm_pinned.restype = None
+        lib.oracle_route.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32, i32, i32, f64, vp, vp, vp, vp, vp]
+        lib.oracle_route.restype = ctypes.c_int
+        lib.oracle_experts.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp, i64, vp]
+        lib.oracle_experts.restype = None
+        lib.oracle_post_residual.argtypes = [vp, vp, i32, vp, f32, i64, i64, f64, vp]
+        lib.oracle_post_residual.restype = None
+        _lib = lib
+    return _lib
+
+
+def _is_bf16(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return 1
+    if a.dtype == np.float32:
+        return 0
+    raise TypeError("expected bf16 bit patterns (uint16) or float32, got %s" % a.dtype)
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    if not a.flags.c_contiguous:
+        raise ValueError("array must be C-contiguous")
+    return a
+
+
+def rmsnorm_pinned(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """Pre-RMSNorm with pinned fp32 rounding: x [T,H] bf16 -> u [T,H] bf16 (uint16)."""
+    x = _c(x)
+    if x.dtype != np.uint16:
+        raise TypeError("pinned RMSNorm takes bf16 input")
+    T, H = x.shape
+    g = np.ascontiguousarray(gain, dtype=np.float32)
+    u = np.empty_like(x)
+    _load().oracle_rmsnorm_pinned(x.ctypes.data, g.ctypes.data, eps, T, H, u.ctypes.data)
+    return u
+
+
+class Routing:
+    """idx [T,K] int32 (decision order), w [T,K] fp64, logits [T,E] fp64 or None,
+    margin [T,2] fp64 (group, expert) or None, agree [T] int32 or None."""
+
+    def __init__(self, idx, w, logits, margin, agree):
+        self.idx, self.w, self.logits, self.margin, self.agree = idx, w, logits, margin, agree
+
+    def min_margin(self) -> float:
+        return float(np.min(self.margin)) if self.margin is not None and self.margin.size else float("inf")
+
+
+def route(act: np.ndarray, w_router: np.ndarray, bias: np.ndarray, n_group: int, topk_group: int, top_k: int,
+          rho: float = 2.5, want_logits: bool = False, want_margin: bool = True) -> Routing:
+    """Sigmoid group-limited top-k routing (see ``beam_oracle.c`` header, steps 1-5)."""
+    act = _c(act)
+    T, H = act.shape
+    E = w_router.shape[0]
+    wr = np.ascontiguousarray(w_router, dtype=np.float32)
+    b = np.ascontiguousarray(bias, dtype=np.float32)
+    idx = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float64)
+    logits = np.empty((T, E), dtype=np.float64) if want_logits else None
+    margin = np.empty((T, 2), dtype=np.float64) if want_margin else None
+    agree = np.empty((T,), dtype=np.int32) if want_margin else None
+    rc = _load().oracle_route(act.ctypes.data, _is_bf16(act), T, H, wr.ctypes.data, b.ctypes.data, E, n_group,
+                              topk_group, top_k, rho, idx.ctypes.data, w.ctypes.data,
+                              logits.ctypes.data if logits is not None else None,
+                              margin.ctypes.data if margin is not None else None,
+                              agree.ctypes.data if agree is not None else None)
+    if rc != 0:
+        raise ValueError("invalid routing shape")
+    return Routing(idx, w, logits, margin, agree)
+
+
+def experts(act: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, idx: np.ndarray,
+            w: np.ndarray, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """y[n] = sum_j w[t,j] * SwiGLU-expert_{idx[t,j]}(act[t]) for t = tokens[n]; fp64 [n,H]."""
+    act = _c(act)
+    T, H = act.shape
+    E, I, H2 = w_gate.shape
+    assert H2 == H and w_up.shape == (E, I, H) and w_down.shape == (E, H, I)
+    wb = _is_bf16(w_gate)
+    assert _is_bf16(w_up) == wb and _is_bf16(w_down) == wb
+    K = idx.shape[1]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    tok = np.arange(T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+    y = np.empty((tok.size, H), dtype=np.float64)
+    _load().oracle_experts(act.ctypes.data, _is_bf16(act), H, I, _c(w_gate).ctypes.data, _c(w_up).ctypes.data,
+                           _c(w_down).ctypes.data, wb, K, idx.ctypes.data, w.ctypes.data, tok.ctypes.data, tok.size,
+                           y.ctypes.data)
+    return y
+
+
+def post_residual(y: np.ndarray, x: np.ndarray, gain: np.ndarray, eps: float, k: float) -> np.ndarray:
+    """out = sqrt((k-1)/k) x + RMSNorm(y; gain, eps) / sqrt(k), fp64 [n,H]."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    x = _c(x)
+    n, H = y.shape
+    assert x.shape == (n, H)
+    g = np.ascontiguousarray(gain, dtype=np.float32)
+    out = np.empty((n, H), dtype=np.float64)
+    _load().oracle_post_residual(y.ctypes.data, x.ctypes.data, _is_bf16(x), g.ctypes.data, eps, n, H, float(k),
+                                 out.ctypes.data)
+    return out
+
+
+class LayerResult:
+    """Oracle results of one layer call: u (layer input after the optional pre-norm),
+    routing (all tokens), tokens (the token rows evaluated), y (MoE output, fp64 [n,H]),
+    out (final output, fp64 [n,H]; equals y without the sublayer)."""
+
+    def __init__(self, u, routing, tokens, y, out):
+        self.u, self.routing, self.tokens, self.y, self.out = u, routing, tokens, y, out
+
+
+def layer(inp, tokens: Optional[np.ndarray] = None, want_logits: bool = False) -> LayerResult:
+    """The whole layer for ``synth.MoEInputs``; routing on all tokens, experts on ``tokens``."""
+    cfg = inp.cfg
+    u = rmsnorm_pinned(inp.x, inp.pre_gain, cfg.eps) if cfg.sublayer else inp.x
+    r = route(u, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, want_logits=want_logits)
+    tok = np.arange(cfg.T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, tok)
+    out = post_residual(y, np.ascontiguousarray(inp.x[tok]), inp.post_gain, cfg.eps, cfg.residual_k) \
+        if cfg.sublayer else y
+    return LayerResult(u, r, tok, y, out)
