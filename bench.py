@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of one Beam mixture-of-experts layer on one MI355X.
+
+A step is one ``beam_moe_forward`` call (router -> permutation -> gate/up -> down ->
+combine) over one batch of synthetic, seeded tokens already resident in HBM.  The primary
+line is the 8192-token prefill layer; the same run also times the 64-token decode layer
+(``secondary``).  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prefill_t8192]
+  python bench.py --copy-calib 1024      # plain 1 GiB device copy (HBM counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 MI355X (prefill 8192 / decode 64); % MFMA / HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+EXPERTS_SRC = os.path.join(ROOT, "sparse_moe_layer_04_amd", "csrc", "experts.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(EXPERTS_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def gate_up_work(cfg, n_touched):
+    """Algorithmic flops and bytes of one gate/up launch.
+
+    flops: 4*H*I per routed pair (gate and up products).
+    bytes: each touched expert's gate and up matrices once (2*I*H bf16), each token row
+    once (H bf16), each h row written once (I bf16)."""
+    P = cfg.T * cfg.top_k
+    flops = 4.0 * cfg.H * cfg.I * P
+    nbytes = n_touched * 2.0 * cfg.I * cfg.H * 2 + cfg.T * cfg.H * 2.0 + P * cfg.I * 2.0
+    return flops, nbytes
+
+
+def down_work(cfg, n_touched):
+    """flops 2*H*I per pair; bytes: each touched W_d once, each h row read, each output row written."""
+    P = cfg.T * cfg.top_k
+    return 2.0 * cfg.H * cfg.I * P, n_touched * cfg.H * cfg.I * 2.0 + P * (cfg.I + cfg.H) * 2.0
+
+
+def roofline(flops, nbytes, seconds, traffic=None):
+    t_f = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_b = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_f >= t_b:
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic}
+    ach = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+            "traffic": traffic}
+
+
+def load_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter runs, or None when the kernel
+    source changed since they were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            d = json.load(f)
+        ent = d[workload]
+        if ent.get("experts_hip_sha256_16") != kernel_source_hash():
+            return None
+        return {"fetch_bytes": ent["fetch_bytes"], "write_bytes": ent["write_bytes"],
+                "bytes": ent["fetch_bytes"] + ent["write_bytes"], "source": os.path.relpath(TRAFFIC_JSON, ROOT)}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def run_workload(cfg, hw, dw, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sparse_moe_layer_04_amd as bm
+    from synth.configs import make_inputs
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    inp = make_inputs(cfg, weights=hw)
+    shape = bm.make_shape(cfg.T, cfg.H, cfg.E, cfg.I, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, cfg.dtype)
+    op = bm.OP_FORWARD_SUBLAYER if cfg.sublayer else bm.OP_FORWARD
+    ws = torch.empty(bm.workspace_size(shape, op), dtype=torch.uint8, device="cuda")
+    x, bias = dev(inp.x), dev(inp.bias)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device="cuda")
+    sub = None
+    if cfg.sublayer:
+        g1, g2 = dev(inp.pre_gain), dev(inp.post_gain)
+        sub = bm.sublayer(g1, g2, cfg.eps, cfg.residual_k)
+    timers = [bm.StageTimer() for _ in range(steps)]
+
+    def step(timer=None):
+        bm.forward(shape, x, dw[0], bias, dw[1], dw[2], dw[3], out, ws, sublayer=sub, topk_idx=idx,
+                   stage_events=timer.events if timer else None)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step(timers[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    stage = np.array([t.elapsed_ms() for t in timers]).mean(axis=0)
+    for t in timers:
+        t.close()
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.E)
+    n_touched = int((counts > 0).sum())
+    return dict(ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage, counts=counts, n_touched=n_touched)
+
+
+def summarize(cfg, r, steps, warmup):
+    ms = r["ms_per_step"]
+    P = cfg.T * cfg.top_k
+    gu_ms = float(r["stage_ms"][4])
+    dn_ms = float(r["stage_ms"][5])
+    gu_f, gu_b = gate_up_work(cfg, r["n_touched"])
+    dn_f, dn_b = down_work(cfg, r["n_touched"])
+    layer_flops = 6.0 * cfg.H * cfg.I * P
+    weight_bytes = r["n_touched"] * 3.0 * cfg.H * cfg.I * 2
+    layer_bytes = weight_bytes + cfg.E * cfg.H * 4.0 + 2.0 * cfg.T * cfg.H * 2
+    import sparse_moe_layer_04_amd as bm
+    return {
+        "tokens_per_s": cfg.T / (ms / 1e3),
+        "ms_per_step": ms,
+        "stages_ms": {n: round(float(v), 4) for n, v in zip(bm.STAGE_NAMES, r["stage_ms"])},
+        "layer": {"tflops": layer_flops / (ms / 1e3) / 1e12, "mfma_frac": layer_flops / (ms / 1e3) / 1e12 /
+                  PEAK_BF16_TFLOPS, "alg_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms / 1e3) / 1e9,
+                  "hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "gate_up": roofline(gu_f, gu_b, gu_ms / 1e3, load_traffic(cfg.name)),
+        "down": roofline(dn_f, dn_b, dn_ms / 1e3),
+        "experts_touched": r["n_touched"],
+        "max_expert_load": int(r["counts"].max()),
+        "empty_experts": int((r["counts"] == 0).sum()),
+    }
+
+
+def cpu_baseline(cfg, hw, n_tokens):
+    """The oracle, as it stands, on a seeded sample of the workload's tokens."""
+    import oracle
+    import synth
+    from synth.configs import make_inputs
+    inp = make_inputs(cfg, weights=hw)
+    tok = synth.subset(cfg.seed_base + 555, 98, cfg.T, n_tokens)
+    t0 = time.perf_counter()
+    x = inp.x[tok]
+    u = oracle.rmsnorm_pinned(x, inp.pre_gain, cfg.eps) if cfg.sublayer else x
+    r = oracle.route(u, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, want_margin=False)
+    y = oracle.experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w)
+    if cfg.sublayer:
+        oracle.post_residual(y, x, inp.post_gain, cfg.eps, cfg.residual_k)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "%d seeded tokens of %s (router + experts%s), %.1f s" % (
+                n_tokens, cfg.name, " + norms" if cfg.sublayer else "", dt)}
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_t8192",
+                    choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768"])
+    ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
+    ap.add_argument("--cpu-tokens", type=int, default=384, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: the layer is built and timed on a single GPU "
+              "(no sharding, no collectives); --gpus %d is not supported" % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return
+    import sparse_moe_layer_04_amd  # noqa: F401  (fails loudly without the HIP library)
+    from synth.configs import CONFIGS, expert_weights
+
+    cfg = CONFIGS[args.workload]
+    t0 = time.time()
+    hw = expert_weights(cfg)
+    log("weights generated in %.1fs" % (time.time() - t0))
+
+    def dev(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    dw = tuple(dev(a) for a in hw)
+    torch.cuda.synchronize()
+    log("weights uploaded")
+
+    prim = run_workload(cfg, hw, dw, args.steps, args.warmup)
+    s = summarize(cfg, prim, args.steps, args.warmup)
+    log("primary %s: %.3f ms/step" % (cfg.name, s["ms_per_step"]))
+    line = {
+        "metric": METRIC,
+        "value": s["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "n_group": cfg.n_group,
+                   "topk_group": cfg.topk_group, "top_k": cfg.top_k, "routed_scaling": cfg.rho,
+                   "sublayer": cfg.sublayer, "parallelism": "single GPU"},
+        "roofline": dict(s["gate_up"], kernel="gate_up (grouped gate/up GEMM + SwiGLU)"),
+        "layer": s["layer"],
+        "stages_ms": s["stages_ms"],
+        "down": s["down"],
+        "experts_touched": s["experts_touched"],
+        "max_expert_load": s["max_expert_load"],
+        "empty_experts": s["empty_experts"],
+    }
+    if args.secondary and args.secondary != "none" and args.secondary != cfg.name:
+        c2 = CONFIGS[args.secondary]
+        r2 = run_workload(c2, hw, dw, args.steps, args.warmup)
+        s2 = summarize(c2, r2, args.steps, args.warmup)
+        log("secondary %s: %.3f ms/step" % (c2.name, s2["ms_per_step"]))
+        line["secondary"] = {"workload": c2.name, "tokens_per_s": s2["tokens_per_s"],
+                             "ms_per_step": s2["ms_per_step"], "layer": s2["layer"], "stages_ms": s2["stages_ms"],
+                             "roofline": dict(s2["gate_up"], kernel="gate_up"), "down": s2["down"],
+                             "experts_touched": s2["experts_touched"]}
+    del dw
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, hw, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,8 +55,15 @@ def _load():
         lib.oracle_experts.restype = None
         lib.oracle_post_residual.argtypes = [vp, vp, i32, vp, f32, i64, i64, f64, vp]
         lib.oracle_post_residual.restype = None
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().oracle_threads())
 
 
 def _is_bf16(a: np.ndarray) -> int:
@@ -150,6 +157,32 @@ def post_residual(y: np.ndarray, x: np.ndarray, gain: np.ndarray, eps: float, k:
     _load().oracle_post_residual(y.ctypes.data, x.ctypes.data, _is_bf16(x), g.ctypes.data, eps, n, H, float(k),
                                  out.ctypes.data)
     return out
+
+
+def permutation(idx: np.ndarray, E: int):
+    """Stable counting sort of the (token, choice) pairs by expert, in plain loops.
+
+    Pair p = t*K + j goes to expert idx[t, j].  Returns (offsets [E+1], sorted_pairs [P],
+    pair_pos [P]): offsets[e] = number of pairs with expert < e; sorted_pairs lists the
+    pairs expert by expert, ascending p within an expert; pair_pos[p] = position of p.
+    Expert e's rows of the grouped products are sorted_pairs[offsets[e]:offsets[e+1]].
+    """
+    flat = [int(v) for v in np.asarray(idx).reshape(-1)]
+    counts = [0] * E
+    for e in flat:
+        counts[e] += 1
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + counts[e])
+    cursor = offsets[:-1]
+    sorted_pairs = [0] * len(flat)
+    pair_pos = [0] * len(flat)
+    for p, e in enumerate(flat):
+        sorted_pairs[cursor[e]] = p
+        pair_pos[p] = cursor[e]
+        cursor[e] += 1
+    return (np.array(offsets, dtype=np.int32), np.array(sorted_pairs, dtype=np.int32),
+            np.array(pair_pos, dtype=np.int32))
 
 
 class LayerResult:

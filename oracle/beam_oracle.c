@@ -45,6 +45,7 @@
  * Tensors: bf16 arrives as uint16 bit patterns and is widened exactly.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -299,3 +300,6 @@ void oracle_post_residual(const double* y, const void* x, int x_bf16, const floa
             out[t * H + h] = a * elem(x, t * H + h, x_bf16) + b * ((double)gain[h] * yr[h] * r);
     }
 }
+
+/* threads the oracle's parallel loops use */
+int oracle_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,169 @@
+// Weighted combine, sandwich RMSNorms and the depth-scaled residual of the Beam MoE
+// layer on gfx950.
+//
+// Combine: y_t = sum_j w_{t,j} z_{t,j}, j ascending (expert outputs combined with the
+// normalised, scaled router weights; Glonce, "Reflection releases Beam, a 501B open
+// MoE model with 1M context", architecture paragraph).
+// Sublayer: RMSNorm before and after the block and the residual update
+// x <- sqrt((k-1)/k) x + block(x)/sqrt(k) (Glonce, residual paragraph; transformers
+// "Beam" model doc, Overview, "Sandwich norms with depth-scaled residuals"); RMSNorm
+// scaling in FP32 (model doc, numerics paragraph).
+#include "common.hpp"
+
+#include <math.h>
+
+namespace beam {
+
+constexpr int CMB_THREADS = 256;
+constexpr int CMB_MAX_K = 32;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
+    __syncthreads();
+    return s;
+}
+
+// bf16 path: 8 consecutive features per step (16-byte loads).  With POST the summed
+// row is kept in LDS (H floats) for the post-norm pass.
+template <bool POST>
+__global__ void __launch_bounds__(CMB_THREADS) combine_bf16_kernel(const uint16_t* __restrict__ y_pair,
+                                                                   const float* __restrict__ topk_w, int H, int K,
+                                                                   const uint16_t* __restrict__ x,
+                                                                   const float* __restrict__ g2, float eps,
+                                                                   float coef_x, float coef_y,
+                                                                   uint16_t* __restrict__ out,
+                                                                   uint16_t* __restrict__ moe_y) {
+    extern __shared__ float ys[];
+    __shared__ float wk[CMB_MAX_K];
+    __shared__ float red[CMB_THREADS / 64];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < K) wk[tid] = topk_w[t * K + tid];
+    __syncthreads();
+    const int nch = H / 8;
+    float ss = 0.f;
+    for (int c = tid; c < nch; c += CMB_THREADS) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        for (int j = 0; j < K; ++j) {
+            const u32x4 v = *(const u32x4*)(y_pair + ((t * K + j) * H + c * 8));
+            const float wj = wk[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(wj, __uint_as_float(v[q] << 16), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(wj, __uint_as_float(v[q] & 0xFFFF0000u), acc[2 * q + 1]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        if (POST) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                ys[c * 8 + q] = acc[q];
+                ss = fmaf(acc[q], acc[q], ss);
+            }
+            if (moe_y) *(u32x4*)(moe_y + t * H + c * 8) = o;
+        } else {
+            *(u32x4*)(out + t * H + c * 8) = o;
+        }
+    }
+    if (!POST) return;
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int c = tid; c < nch; c += CMB_THREADS) {
+        const u32x4 xv = *(const u32x4*)(x + t * H + c * 8);
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float xq = q & 1 ? __uint_as_float(xv[q >> 1] & 0xFFFF0000u) : __uint_as_float(xv[q >> 1] << 16);
+            const float yh = g2[c * 8 + q] * (ys[c * 8 + q] * r);
+            o[q] = fmaf(coef_x, xq, coef_y * yh);
+        }
+        u32x4 ov;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ov[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+        *(u32x4*)(out + t * H + c * 8) = ov;
+    }
+}
+
+// fp32 path: one feature per step, no sublayer.
+__global__ void __launch_bounds__(CMB_THREADS) combine_f32_kernel(const float* __restrict__ y_pair,
+                                                                  const float* __restrict__ topk_w, int H, int K,
+                                                                  float* __restrict__ out) {
+    const int64_t t = blockIdx.x;
+    for (int h = threadIdx.x; h < H; h += CMB_THREADS) {
+        float acc = 0.f;
+        for (int j = 0; j < K; ++j) acc = fmaf(topk_w[t * K + j], y_pair[(t * K + j) * H + h], acc);
+        out[t * H + h] = acc;
+    }
+}
+
+hipError_t launch_combine(const void* y_pair, bool bf16, const float* topk_w, int64_t T, int H, int K, const void* x,
+                          const float* post_gain, float eps, float residual_k, void* out, void* moe_y,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (!bf16) {
+        combine_f32_kernel<<<(unsigned)T, CMB_THREADS, 0, s>>>((const float*)y_pair, topk_w, H, K, (float*)out);
+    } else if (post_gain == nullptr) {
+        combine_bf16_kernel<false><<<(unsigned)T, CMB_THREADS, 0, s>>>(
+            (const uint16_t*)y_pair, topk_w, H, K, nullptr, nullptr, 0.f, 0.f, 0.f, (uint16_t*)out, nullptr);
+    } else {
+        const double k = (double)residual_k;
+        const float cx = (float)sqrt((k - 1.0) / k);
+        const float cy = (float)(1.0 / sqrt(k));
+        combine_bf16_kernel<true><<<(unsigned)T, CMB_THREADS, (size_t)H * sizeof(float), s>>>(
+            (const uint16_t*)y_pair, topk_w, H, K, (const uint16_t*)x, post_gain, eps, cx, cy, (uint16_t*)out,
+            (uint16_t*)moe_y);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Pre-RMSNorm with pinned rounding: the mean square is summed in fp64 (squares of
+// bf16 values are exact in fp64), r = fp32(1/sqrt(ss/H + eps)) is evaluated in fp64
+// and rounded once, then u = bf16(fp32(fp32(x*r) * g)).  Every step is correctly
+// rounded, so u does not depend on the summation order except in the last fp64 bit
+// of ss.
+// ---------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rmsnorm_pinned_kernel(const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ gain, float eps, int H,
+                                                             uint16_t* __restrict__ u) {
+    __shared__ double red[256];
+    __shared__ float r_sh;
+    const int64_t t = blockIdx.x;
+    const uint16_t* xr = x + t * H;
+    double ss = 0.0;
+    for (int h = threadIdx.x; h < H; h += 256) {
+        const double v = (double)bf16_to_f32(xr[h]);
+        ss += v * v;
+    }
+    red[threadIdx.x] = ss;
+    __syncthreads();
+    for (int n = 128; n >= 1; n >>= 1) {
+        if ((int)threadIdx.x < n) red[threadIdx.x] += red[threadIdx.x + n];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) r_sh = (float)(1.0 / sqrt(red[0] / (double)H + (double)eps));
+    __syncthreads();
+    const float r = r_sh;
+    for (int h = threadIdx.x; h < H; h += 256) {
+        const float a = __fmul_rn(bf16_to_f32(xr[h]), r);
+        u[t * H + h] = f32_to_bf16(__fmul_rn(a, gain[h]));
+    }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, int64_t T, int H, uint16_t* u,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    rmsnorm_pinned_kernel<<<(unsigned)T, 256, 0, s>>>(x, gain, eps, H, u);
+    return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,87 @@
+// Device helpers and the internal launcher interface of the Beam MoE library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace beam {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// One grouped-GEMM work item: `row_count` consecutive rows of the expert-sorted
+// pair list starting at `row_begin`, all routed to `expert`.
+struct TileEntry {
+    int32_t expert;
+    int32_t row_begin;
+    int32_t row_count;
+    int32_t pad;
+};
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----------------
+
+hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, int64_t T, int H, uint16_t* u,
+                          hipStream_t s);
+
+// logits [T,E] fp32 from activations (bf16 or fp32) and the fp32 router matrix
+hipError_t launch_router_logits(const void* x, bool bf16, const float* w_router, int64_t T, int H, int E,
+                                float* logits, hipStream_t s);
+
+hipError_t launch_router_select(const float* logits, const float* bias, int64_t T, int E, int n_group,
+                                int topk_group, int top_k, float rho, int32_t* idx, float* w, hipStream_t s);
+
+// scratch words the permutation needs for P pairs and E experts
+size_t permute_scratch_words(int64_t P, int E);
+
+// stable counting sort of pairs by expert; when tiles != nullptr also the GEMM
+// work list with at most `tile_rows` rows per tile (count in *num_tiles)
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* scratch, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_pos, TileEntry* tiles, int32_t* num_tiles,
+                          int tile_rows, hipStream_t s);
+
+// upper bound on the number of tiles of at most `tile_rows` rows
+inline int64_t max_tiles(int64_t P, int E, int tile_rows) { return (P + tile_rows - 1) / tile_rows + E; }
+
+// rows per GEMM tile the forward pass uses for a given average load
+int gemm_tile_rows(int64_t P, int E, bool bf16);
+
+// h[row, :] = silu(A W_g^T) * (A W_u^T) for the expert-sorted rows (A = gathered token rows)
+hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int H, int I, int top_k,
+                          const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+                          int64_t max_tile_count, int tile_rows, void* h, hipStream_t s);
+
+// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, int H, int I, const int32_t* sorted_pairs,
+                       const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, int tile_rows,
+                       void* y_pair, hipStream_t s);
+
+// fp32 path (no tiles): one thread per output element
+hipError_t launch_gate_up_f32(const float* act, const float* w_gate, const float* w_up, int H, int I, int top_k,
+                              const int32_t* sorted_pairs, const int32_t* topk_idx, int64_t P, float* h,
+                              hipStream_t s);
+hipError_t launch_down_f32(const float* h, const float* w_down, int H, int I, const int32_t* sorted_pairs,
+                           const int32_t* topk_idx, int64_t P, float* y_pair, hipStream_t s);
+
+// out[t] = sum_j w[t,j] y_pair[t*K + j] (+ post-norm and residual when post_gain != nullptr)
+hipError_t launch_combine(const void* y_pair, bool bf16, const float* topk_w, int64_t T, int H, int K,
+                          const void* x, const float* post_gain, float eps, float residual_k, void* out, void* moe_y,
+                          hipStream_t s);
+
+}  // namespace beam

@@ -1,0 +1,138 @@
+// Token permutation on gfx950: a stable counting sort of (token, choice) pairs by
+// expert, plus the grouped-GEMM work list.
+//
+// Pairs are cut into chunks of PERM_CHUNK.  (1) each chunk counts its experts in LDS;
+// (2) one work-group scans the counts per expert over chunks and over experts, giving
+// every chunk a base row per expert, the expert offsets and the tile list; (3) one
+// wave per chunk walks its pairs in order and ranks equal experts with ballots, so
+// rows inside an expert stay in ascending pair order (deterministic output).
+#include "common.hpp"
+
+namespace beam {
+
+constexpr int PERM_CHUNK = 4096;
+constexpr int PERM_MAX_E = 1024;
+
+size_t permute_scratch_words(int64_t P, int E) {
+    int64_t chunks = (P + PERM_CHUNK - 1) / PERM_CHUNK;
+    if (chunks < 1) chunks = 1;
+    return (size_t)(chunks * E);
+}
+
+__global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                        int32_t* __restrict__ counts) {
+    __shared__ int32_t cnt[PERM_MAX_E];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int64_t p0 = (int64_t)blockIdx.x * PERM_CHUNK;
+    const int64_t p1 = p0 + PERM_CHUNK < P ? p0 + PERM_CHUNK : P;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+        const int e = idx[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One work-group of 1024 threads.
+__global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ counts, int nchunks, int E, int64_t P,
+                                                         int32_t* __restrict__ offsets, TileEntry* __restrict__ tiles,
+                                                         int32_t* __restrict__ num_tiles, int tile_rows) {
+    __shared__ int32_t tot[PERM_MAX_E];
+    __shared__ int32_t off[PERM_MAX_E];
+    __shared__ int32_t ntl[PERM_MAX_E];
+    __shared__ int32_t toff[PERM_MAX_E];
+    const int tid = threadIdx.x;
+    // per expert: exclusive scan over chunks (in place) and the expert total
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            int32_t v = counts[(int64_t)c * E + e];
+            counts[(int64_t)c * E + e] = run;
+            run += v;
+        }
+        tot[e] = run;
+        ntl[e] = run > 0 ? (run + tile_rows - 1) / tile_rows : 0;
+    }
+    __syncthreads();
+    // exclusive scans over experts (E <= 1024: a single pass by one thread is cheap)
+    if (tid == 0) {
+        int32_t a = 0, b = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = a;
+            a += tot[e];
+            toff[e] = b;
+            b += ntl[e];
+        }
+        offsets[E] = a;
+        if (num_tiles) *num_tiles = b;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        offsets[e] = off[e];
+        for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += off[e];
+        if (tiles) {
+            int n = ntl[e];
+            if (n > 0) {
+                int c = tot[e];
+                int r = (c + n - 1) / n;  // balanced rows per tile, <= tile_rows
+                for (int j = 0; j < n; ++j) {
+                    TileEntry te;
+                    te.expert = e;
+                    te.row_begin = off[e] + j * r;
+                    te.row_count = (c - j * r) < r ? (c - j * r) : r;
+                    te.pad = 0;
+                    tiles[toff[e] + j] = te;
+                }
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                          const int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ pair_pos) {
+    __shared__ int32_t next[PERM_MAX_E];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) next[e] = base[(int64_t)blockIdx.x * E + e];
+    __syncthreads();
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t p0 = (int64_t)blockIdx.x * PERM_CHUNK;
+    const int64_t p1 = p0 + PERM_CHUNK < P ? p0 + PERM_CHUNK : P;
+    for (int64_t pb = p0; pb < p1; pb += 64) {
+        const int64_t p = pb + lane;
+        int e = p < p1 ? idx[p] : -1;
+        const bool valid = e >= 0 && e < E;  // out-of-range ids are skipped
+        if (!valid) e = 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < ebits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        if (valid) {
+            const int rank = __popcll(peers & lt_mask);
+            const int32_t dest = next[e] + rank;
+            sorted_pairs[dest] = (int32_t)p;
+            pair_pos[p] = dest;
+            // the highest lane of the peer group advances the expert's cursor
+            if ((peers >> lane) == 1ull) next[e] += __popcll(peers);
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* scratch, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_pos, TileEntry* tiles, int32_t* num_tiles,
+                          int tile_rows, hipStream_t s) {
+    int nchunks = (int)((P + PERM_CHUNK - 1) / PERM_CHUNK);
+    if (nchunks > 0) perm_hist_kernel<<<nchunks, 256, 0, s>>>(idx, P, E, scratch);
+    perm_scan_kernel<<<1, 1024, 0, s>>>(scratch, nchunks, E, P, offsets, tiles, num_tiles, tile_rows);
+    if (nchunks > 0) perm_scatter_kernel<<<nchunks, 64, 0, s>>>(idx, P, E, scratch, sorted_pairs, pair_pos);
+    return hipGetLastError();
+}
+
+}  // namespace beam

@@ -348,6 +348,33 @@ def test_residual_special_cases():
     np.testing.assert_allclose(out1, g.astype(np.float64) * y / rms, rtol=1e-12)
 
 
+# ----------------------------------------------------------------------------- permutation
+
+def test_permutation_is_the_stable_counting_sort():
+    rng = np.random.default_rng(4)
+    for T, K, E in ((1, 1, 1), (7, 3, 5), (50, 8, 16), (300, 8, 64)):
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+        off, srt, pos = oracle.permutation(idx, E)
+        flat = idx.reshape(-1)
+        # textbook identities: exclusive scan of the histogram; stable argsort; inverse map
+        np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        np.testing.assert_array_equal(srt, np.argsort(flat, kind="stable"))
+        assert sorted(srt.tolist()) == list(range(T * K))
+        np.testing.assert_array_equal(srt[pos], np.arange(T * K))
+        for e in range(E):
+            seg = srt[off[e]:off[e + 1]]
+            assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()
+
+
+def test_permutation_brute_force_tiny():
+    # every assignment of 4 pairs to 3 experts
+    for code in range(3 ** 4):
+        idx = np.array([(code // 3 ** i) % 3 for i in range(4)], np.int32).reshape(2, 2)
+        off, srt, pos = oracle.permutation(idx, 3)
+        expect = [p for e in range(3) for p in range(4) if idx.reshape(-1)[p] == e]
+        assert srt.tolist() == expect
+
+
 # ----------------------------------------------------------------------------- page figures
 
 def test_expert_structure_matches_printed_parameter_counts():
