@@ -30,7 +30,8 @@
  *   - Results are deterministic: a call with the same inputs gives bitwise the
  *     same outputs.
  *   - Concurrent calls must not share a workspace.
- *   - T = 0 is a valid no-op.
+ *   - T = 0 is a valid no-op (no workspace needed; beam_moe_permute then only
+ *     zeroes `offsets`).
  */
 #ifndef BEAM_MOE_H
 #define BEAM_MOE_H
@@ -134,9 +135,10 @@ beam_status beam_moe_rmsnorm(const beam_moe_shape* shape, const void* x, const f
  *   logits_out [T,E] fp32 out, optional (the router logits before the sigmoid)
  *   ws       scratch of beam_moe_workspace_size(BEAM_OP_ROUTE) bytes; may be NULL
  *            (ws_bytes 0) when logits_out is given.
- * Logits are accumulated with exact bf16 x bf16 partial products in fp32 blocks
- * of 256 terms summed in fp64, then rounded to fp32; s, s', group scores and all
- * comparisons are fp32.
+ * Logits are accumulated from exact bf16 x bf16 partial products: each 32-term
+ * block is summed on the matrix cores in fp32, the blocks are summed in fp64, and
+ * the logit is rounded once to fp32; s, s', group scores and all comparisons are
+ * fp32.
  */
 beam_status beam_moe_route(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
                            int32_t* topk_idx, float* topk_w, float* logits_out, void* ws, size_t ws_bytes,

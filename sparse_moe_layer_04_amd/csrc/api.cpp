@@ -126,13 +126,13 @@ beam_status beam_moe_route(const beam_moe_shape* shape, const void* x, const flo
     if (!shape_valid(shape) || !x || !w_router || !bias || !topk_idx || !topk_w) return BEAM_ERR_INVALID_ARG;
     if (!shape_supported(shape)) return BEAM_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_router)) return BEAM_ERR_INVALID_ARG;
+    if (shape->T == 0) return BEAM_OK;
     float* logits = logits_out;
     if (!logits) {
         const Layout L = make_layout(shape, BEAM_OP_ROUTE);
         if (!ws || ws_bytes < L.total) return BEAM_ERR_WORKSPACE;
         logits = at<float>(ws, L.logits);
     }
-    if (shape->T == 0) return BEAM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = shape->dtype == BEAM_BF16;
     hipError_t e = beam::launch_router_logits(x, bf16, w_router, shape->T, shape->H, shape->E, logits, s);
@@ -144,6 +144,9 @@ beam_status beam_moe_route(const beam_moe_shape* shape, const void* x, const flo
 beam_status beam_moe_permute(const beam_moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
                              int32_t* sorted_pairs, int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream) {
     if (!shape_valid(shape) || !topk_idx || !offsets || !sorted_pairs || !pair_pos) return BEAM_ERR_INVALID_ARG;
+    if (shape->T == 0)  // no pairs: the scan alone writes the all-zero offsets
+        return hip_status(beam::launch_permute(topk_idx, 0, shape->E, nullptr, offsets, sorted_pairs, pair_pos,
+                                               nullptr, nullptr, 1, static_cast<hipStream_t>(stream)));
     const Layout L = make_layout(shape, BEAM_OP_PERMUTE);
     if (!ws || ws_bytes < L.total) return BEAM_ERR_WORKSPACE;
     const int64_t P = shape->T * shape->top_k;
@@ -169,9 +172,9 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
     if (stage_events)
         for (int i = 0; i <= BEAM_NUM_STAGES; ++i)
             if (!stage_events[i]) return BEAM_ERR_INVALID_ARG;
+    if (shape->T == 0) return BEAM_OK;  // nothing to do: no workspace needed
     const Layout L = make_layout(shape, sub ? BEAM_OP_FORWARD_SUBLAYER : BEAM_OP_FORWARD);
     if (!ws || ws_bytes < L.total) return BEAM_ERR_WORKSPACE;
-    if (shape->T == 0) return BEAM_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t T = shape->T, P = T * shape->top_k;

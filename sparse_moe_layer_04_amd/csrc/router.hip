@@ -17,8 +17,8 @@ namespace beam {
 // ---------------------------------------------------------------------------------
 // Logits for bf16 activations.  Each fp32 router weight is split exactly into three
 // bf16 parts (hi + mid + lo, by truncation), so every MFMA product x*part is exact
-// in fp32.  MFMA accumulates 256-term blocks in fp32; the blocks are summed in fp64
-// and the logit is rounded once to fp32.
+// in fp32.  MFMA sums each 32-term block (lo, mid, then hi parts) in fp32; the
+// blocks are summed in fp64 and the logit is rounded once to fp32.
 //
 // Work-group: 4 waves, 32 tokens x 128 experts; wave w owns experts [32w, 32w+32).
 // Operands are read straight from global memory (the matrix is L2-resident).
@@ -97,13 +97,13 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bh, acc[rb][cb], 0, 0, 0);
             }
         }
-        if ((ks & 7) == 7 || ks == nks - 1) {  // fold a 256-term block into fp64
-            for (int i = 0; i < 2; ++i)
-                for (int j = 0; j < 2; ++j) {
-                    for (int q = 0; q < 4; ++q) acc64[i][j][q] += (double)acc[i][j][q];
-                    acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-        }
+        // fold each 32-term block into fp64: the matrix-core sum rounds once per
+        // instruction, so short fp32 chains keep the logit error near one fp32 ulp
+        for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) {
+                for (int q = 0; q < 4; ++q) acc64[i][j][q] += (double)acc[i][j][q];
+                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
     }
     // C layout of a 16x16 MFMA block: lane holds rows 4*(lane>>4)+q, column lane&15
     for (int rb = 0; rb < 2; ++rb)

@@ -163,7 +163,11 @@ def test_forward_is_deterministic_and_t0_noop():
     out = torch.empty((1, cfg.H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(1, dtype=torch.uint8, device="cuda")
     bm.forward(s0, d.x, d.wr, d.bias, d.wg, d.wu, d.wd, out, ws)
+    off = torch.full((cfg.E + 1,), 7, dtype=torch.int32, device="cuda")
+    dummy = torch.empty(1, dtype=torch.int32, device="cuda")
+    bm.permute(s0, dummy, off, dummy, dummy, None)
     torch.cuda.synchronize()
+    assert not off.any()
 
 
 def test_identical_experts_closed_form():
