@@ -60,7 +60,8 @@ typedef enum beam_dtype { BEAM_F32 = 0, BEAM_BF16 = 1 } beam_dtype;
  * Layer shape.  Limits: T >= 0, T * top_k < 2^31; 1 <= E <= 1024;
  * E % n_group == 0; E / n_group <= 1024; 1 <= n_group <= 64;
  * 1 <= topk_group <= n_group; 1 <= top_k <= min(32, topk_group * E / n_group);
- * H, I >= 1.  BEAM_BF16 additionally needs H % 128 == 0 and I % 128 == 0.
+ * H, I >= 1.  With BEAM_BF16, beam_moe_forward needs H % 256 == 0 and
+ * I % 128 == 0, and beam_moe_route needs H % 32 == 0 (else BEAM_ERR_UNSUPPORTED).
  * Beam: H = 5120, E = 256, I = 2560, n_group = 8, topk_group = 4, top_k = 8,
  * routed_scaling = 2.5.
  */

@@ -27,8 +27,11 @@ bool shape_valid(const beam_moe_shape* s) {
     return true;
 }
 
+// bf16 kernels: the router sweeps H in 32-wide MFMA steps; the expert GEMMs sweep K in
+// 128-wide unrolled groups and cover N in 128 (gate/up) or 256 (down) column blocks.
+bool route_supported(const beam_moe_shape* s) { return s->dtype != BEAM_BF16 || s->H % 32 == 0; }
 bool shape_supported(const beam_moe_shape* s) {
-    if (s->dtype == BEAM_BF16) return s->H % 128 == 0 && s->I % 128 == 0;
+    if (s->dtype == BEAM_BF16) return s->H % 256 == 0 && s->I % 128 == 0;
     return true;
 }
 
@@ -103,7 +106,8 @@ const char* beam_status_string(beam_status st) {
 beam_status beam_moe_workspace_size(const beam_moe_shape* shape, int32_t op, size_t* bytes) {
     if (!bytes || !shape_valid(shape) || op < BEAM_OP_ROUTE || op > BEAM_OP_FORWARD_SUBLAYER)
         return BEAM_ERR_INVALID_ARG;
-    if (!shape_supported(shape)) return BEAM_ERR_UNSUPPORTED;
+    if (op == BEAM_OP_ROUTE ? !route_supported(shape) : (op != BEAM_OP_PERMUTE && !shape_supported(shape)))
+        return BEAM_ERR_UNSUPPORTED;
     if (op == BEAM_OP_FORWARD_SUBLAYER && shape->dtype != BEAM_BF16) return BEAM_ERR_UNSUPPORTED;
     *bytes = make_layout(shape, op).total;
     return BEAM_OK;
@@ -124,7 +128,7 @@ beam_status beam_moe_route(const beam_moe_shape* shape, const void* x, const flo
                            int32_t* topk_idx, float* topk_w, float* logits_out, void* ws, size_t ws_bytes,
                            void* stream) {
     if (!shape_valid(shape) || !x || !w_router || !bias || !topk_idx || !topk_w) return BEAM_ERR_INVALID_ARG;
-    if (!shape_supported(shape)) return BEAM_ERR_UNSUPPORTED;
+    if (!route_supported(shape)) return BEAM_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_router)) return BEAM_ERR_INVALID_ARG;
     if (shape->T == 0) return BEAM_OK;
     float* logits = logits_out;

@@ -8,25 +8,159 @@
 //   down:     y_pair[p, :] = h[r, :] W_d[e]^T
 // where row r of the expert-sorted pair list holds pair p = t*top_k + j routed to e.
 //
-// bf16 path: one work-group computes one (tile, column block): up to BM rows of one
-// expert times BN weight rows, K swept in steps of BK through LDS with a register
-// prefetch of the next step.  Gate/up tiles hold BN/2 gate rows and BN/2 up rows of
-// the same output columns, so the SwiGLU epilogue has both operands in registers.
-// The gate/up A operand is gathered straight from the token rows (no permuted copy);
-// the down epilogue scatters each row to its pair position.
+// bf16 path (details below): one work-group computes one (tile, column block) on
+// MFMA.  Gate/up column blocks hold the gate and the up rows of the same output
+// columns, so the SwiGLU epilogue has both operands in registers.  The gate/up A
+// operand is gathered straight from the token rows (no permuted copy); the down
+// epilogue scatters each row to its pair position.
 #include "common.hpp"
+
+#include <type_traits>
 
 namespace beam {
 
-constexpr int GBK = 64;    // k per LDS stage
-constexpr int GBN = 128;   // weight rows per tile
-constexpr int GTHREADS = 256;
+// ---------------------------------------------------------------------------------
+// bf16 grouped GEMM on MFMA (16x16x32, fp32 accumulation).
+//
+// Work item: (tile, column block).  A tile is up to GROWS = 288 consecutive rows of the
+// expert-sorted pair list, all routed to one expert (row_count may be smaller; 16-row
+// blocks past it are skipped).  A column block is 128 h columns (gate/up: 8 waves x
+// (16 gate + 16 up weight rows)) or 256 output columns (down: 8 waves x 32 weight
+// rows).  Each wave owns its weight rows: they stream from HBM straight into
+// registers, never through LDS.  All waves share the tile's activation rows
+// through an LDS double buffer.  K is swept 32 at a time; global loads of both
+// operands run 3 steps ahead in a ring of 4 register sets (one VMEM counter orders
+// both streams, so they share the prefetch distance).
+// ---------------------------------------------------------------------------------
+constexpr int GROWS = 288;    // rows per tile: at 8192 tokens almost every expert fits one tile
+constexpr int GRB = GROWS / 16;
+constexpr int GKS = 32;       // k per step (one MFMA)
+constexpr int GWAVES = 8;
+constexpr int GTHREADS = GWAVES * 64;
+constexpr int GRING = 4;      // register sets: 3 steps in flight + 1 in use
 
-// LDS element offset of 16-byte chunk `ch` (0..7) of tile row `row`; the XOR spreads the
-// 16 rows read by one MFMA operand load over distinct banks.
-__device__ __forceinline__ int lds_off(int row, int ch) { return row * GBK + ((ch ^ (row & 7)) << 3); }
+// LDS element offset of 16-byte chunk `ch` (0..3) of activation row `row` (64-byte rows).
+// The MFMA operand read (lane -> row lane&15, chunk lane>>4) and the staging write are
+// free of bank conflicts on gfx950 with this XOR (measured with the LDS bank-conflict
+// counter over candidate layouts).
+__device__ __forceinline__ int a_off(int row, int ch) { return row * GKS + ((ch ^ ((row >> 1) & 3)) << 3); }
 
-template <int BM, int WM, bool GATED>
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Per-tile context shared by the row-count variants of the main loop.
+struct TileCtx {
+    const uint16_t* A;    // activations (gate/up: token rows, gathered) or h (down)
+    const uint16_t* bp0;  // this lane's first weight row (k offset applied)
+    const uint16_t* bp1;  // second weight row block (up rows, or the next 16 down rows)
+    int K, nk, top_k;     // reduction length, its 32-wide steps, routes per token
+    int row_begin, row_count, ccol, N;
+    const int32_t* sorted_pairs;
+    uint16_t* C;
+};
+
+// Main loop and epilogue for tiles of at most NRB 16-row blocks, with global loads
+// RING - 1 steps ahead.  Every load and store is unconditional (clamped addresses), so
+// the steady state has no branches and the compiler's memory-counter waits stay exact.
+// Only the NRB*16 activation rows the variant reads are loaded: thread t stages chunk
+// (t + 512 i) mod (NRB*64), so small tiles reload (cached) chunks instead of branching.
+template <bool GATED, int NRB, int RING>
+__device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
+    constexpr int ACH = NRB * 64;                          // 16-byte activation chunks per step
+    constexpr int AL = (ACH + GTHREADS - 1) / GTHREADS;    // activation loads per thread per step
+    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const uint16_t* ap[AL];
+    int alds[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int q = (tid + i * GTHREADS) % ACH;
+        const int row = q >> 2, ch = q & 3;
+        const int src = row < c.row_count ? row : 0;  // rows past the tile read row 0 (never stored)
+        const int64_t arow = GATED ? (int64_t)(c.sorted_pairs[c.row_begin + src] / c.top_k)
+                                   : (int64_t)(c.row_begin + src);
+        ap[i] = c.A + arow * c.K + ch * 8;
+        alds[i] = a_off(row, ch);
+    }
+
+    u32x4 ra[RING][AL], rb[RING][2];
+    f32x4 acc[NRB][2];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = c.nk;
+    auto load = [&](int kstep, int set) {
+        const int k0 = (kstep < nk ? kstep : nk - 1) * GKS;  // past the end: reload the last step
+#pragma unroll
+        for (int i = 0; i < AL; ++i) ra[set][i] = *(const u32x4*)(ap[i] + k0);
+        rb[set][0] = *(const u32x4*)(c.bp0 + k0);
+        rb[set][1] = *(const u32x4*)(c.bp1 + k0);
+    };
+    auto store_a = [&](int set, int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) *(u32x4*)(&lds[buf][alds[i]]) = ra[set][i];
+    };
+    const int rd_row = lane & 15, rd_ch = lane >> 4;
+    auto compute = [&](int set, int buf) {
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, rb[set][0]);
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, rb[set][1]);
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            const bf16x8 a = *(const bf16x8*)(&lds[buf][a_off(r * 16 + rd_row, rd_ch)]);
+            acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[r][0], 0, 0, 0);
+            acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[r][1], 0, 0, 0);
+        }
+    };
+    // one K step; `j` (= kt % RING) is a compile-time constant in the unrolled loop
+    auto step = [&](int kt, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        load(kt + RING - 1, (j + RING - 1) % RING);
+        compute(j, j & 1);
+        store_a((j + 1) % RING, (j + 1) & 1);
+        lds_barrier();
+    };
+
+#pragma unroll
+    for (int s = 0; s < RING - 1; ++s) load(s, s);
+    store_a(0, 0);
+    lds_barrier();
+    for (int kt = 0; kt < nk; kt += RING) {  // nk is a multiple of RING
+        step(kt, std::integral_constant<int, 0>());
+        step(kt + 1, std::integral_constant<int, 1>());
+        step(kt + 2, std::integral_constant<int, 2>());
+        step(kt + 3, std::integral_constant<int, 3>());
+        if constexpr (RING == 8) {
+            step(kt + 4, std::integral_constant<int, 4>());
+            step(kt + 5, std::integral_constant<int, 5>());
+            step(kt + 6, std::integral_constant<int, 6>());
+            step(kt + 7, std::integral_constant<int, 7>());
+        }
+    }
+
+    // ---- epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15) ----
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = r * 16 + 4 * (lane >> 4) + q;
+            if (m >= c.row_count) continue;
+            if (GATED) {
+                const float g = acc[r][0][q];
+                const float u = acc[r][1][q];
+                c.C[(int64_t)(c.row_begin + m) * c.N + c.ccol] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+            } else {
+                const int64_t p = c.sorted_pairs[c.row_begin + m];
+                c.C[p * c.N + c.ccol] = f32_to_bf16(acc[r][0][q]);
+                c.C[p * c.N + c.ccol + 16] = f32_to_bf16(acc[r][1][q]);
+            }
+        }
+    }
+}
+
+template <bool GATED>
 __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                  const uint16_t* __restrict__ B0,
                                                                  const uint16_t* __restrict__ B1, int K, int N,
@@ -34,218 +168,102 @@ __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t*
                                                                  const TileEntry* __restrict__ tiles,
                                                                  const int32_t* __restrict__ num_tiles,
                                                                  int n_col_blocks, uint16_t* __restrict__ C) {
-    constexpr int WN = 4 / WM;
-    constexpr int RB = BM / (16 * WM);   // 16-row MFMA blocks per wave
-    constexpr int CB = GBN / (16 * WN);  // 16-column MFMA blocks per wave
-    constexpr int NOUT = GATED ? GBN / 2 : GBN;
-    constexpr int A_CHUNKS = BM * 8;
-    constexpr int A_PER_T = (A_CHUNKS + GTHREADS - 1) / GTHREADS;
-    constexpr int B_PER_T = GBN * 8 / GTHREADS;
-    static_assert(RB >= 1 && CB >= 2 && (CB % 2) == 0, "tile shape");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][GROWS * GKS];
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * GBK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[GBN * GBK];
-
-    const int tile_id = (int)(blockIdx.x / n_col_blocks);
-    const int cblk = (int)(blockIdx.x % n_col_blocks);
-    if (tile_id >= *num_tiles) return;
-    const TileEntry te = tiles[tile_id];
+    // XCD-aware order: blocks are dealt round-robin to the 8 XCDs, so give each XCD a
+    // contiguous run of work items (the column blocks of one tile share its activation
+    // rows in that XCD's L2).
+    const int work = *num_tiles * n_col_blocks;
+    const int per_xcd = (work + 7) >> 3;
+    const int slot = (int)(blockIdx.x >> 3);
+    if (slot >= per_xcd) return;
+    const int item = (int)(blockIdx.x & 7) * per_xcd + slot;
+    if (item >= work) return;
+    const TileEntry te = tiles[item / n_col_blocks];
+    const int cblk = item % n_col_blocks;
     if (te.row_count <= 0) return;
     const int e = te.expert;
-    const int n0 = cblk * NOUT;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave % WM;
-    const int wn = wave / WM;
 
-    // ---- global -> register -> LDS assignments (16-byte chunks) ----
-    const uint16_t* a_src[A_PER_T];
-    int a_lds[A_PER_T];
-    bool a_ok[A_PER_T], a_in[A_PER_T];
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-        const int c = tid + i * GTHREADS;
-        const int row = c >> 3, ch = c & 7;
-        a_in[i] = c < A_CHUNKS;
-        a_ok[i] = a_in[i] && row < te.row_count;
-        int64_t src_row = 0;
-        if (a_ok[i]) {
-            const int srow = te.row_begin + row;
-            src_row = GATED ? (int64_t)(sorted_pairs[srow] / top_k) : (int64_t)srow;
-        }
-        a_src[i] = A + src_row * K + ch * 8;
-        a_lds[i] = lds_off(a_in[i] ? row : 0, ch);
-    }
-    const uint16_t* b_src[B_PER_T];
-    int b_lds[B_PER_T];
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
-        const int c = tid + i * GTHREADS;
-        const int row = c >> 3, ch = c & 7;
-        if (GATED) {
-            const uint16_t* W = row < GBN / 2 ? B0 : B1;
-            b_src[i] = W + ((int64_t)e * N + n0 + (row & (GBN / 2 - 1))) * K + ch * 8;
-        } else {
-            b_src[i] = B0 + ((int64_t)e * N + n0 + row) * K + ch * 8;
-        }
-        b_lds[i] = lds_off(row, ch);
-    }
-
-    u32x4 ra[A_PER_T], rbv[B_PER_T];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i)
-            ra[i] = a_ok[i] ? *(const u32x4*)(a_src[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) rbv[i] = *(const u32x4*)(b_src[i] + k0);
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i)
-            if (a_in[i]) *(u32x4*)(As + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) *(u32x4*)(Bs + b_lds[i]) = rbv[i];
-    };
-
-    f32x4 acc[RB][CB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int wrow0 = wm * RB * 16;
-    bool rb_on[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) rb_on[i] = wrow0 + i * 16 < te.row_count;
-
-    int brow[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        if (GATED)
-            brow[cb] = (cb < CB / 2) ? wn * (CB / 2) * 16 + cb * 16 : GBN / 2 + wn * (CB / 2) * 16 + (cb - CB / 2) * 16;
-        else
-            brow[cb] = wn * CB * 16 + cb * 16;
-    }
-
-    const int nk = K / GBK;
-    gload(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        lstore();
-        __syncthreads();
-        if (kt + 1 < nk) gload((kt + 1) * GBK);
-        if (rb_on[0]) {
-#pragma unroll
-            for (int ks = 0; ks < GBK / 32; ++ks) {
-                const int ch = ks * 4 + (lane >> 4);
-                bf16x8 b[CB];
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) b[cb] = *(const bf16x8*)(Bs + lds_off(brow[cb] + (lane & 15), ch));
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    if (!rb_on[rb]) continue;
-                    const bf16x8 a = *(const bf16x8*)(As + lds_off(wrow0 + rb * 16 + (lane & 15), ch));
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], acc[rb][cb], 0, 0, 0);
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15) ----
+    TileCtx c;
+    c.nk = K / GKS;
+    c.row_begin = te.row_begin;
+    c.row_count = te.row_count;
+    c.N = N;
+    c.sorted_pairs = sorted_pairs;
+    c.C = C;
+    // weight rows of this wave (two 16-row MFMA operand blocks)
+    int col0;
     if (GATED) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int cb = 0; cb < CB / 2; ++cb) {
-                const int col = n0 + wn * (CB / 2) * 16 + cb * 16 + (lane & 15);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int m = wrow0 + rb * 16 + 4 * (lane >> 4) + q;
-                    if (m < te.row_count) {
-                        const float g = acc[rb][cb][q];
-                        const float u = acc[rb][cb + CB / 2][q];
-                        const float hv = g / (1.0f + __expf(-g)) * u;
-                        C[(int64_t)(te.row_begin + m) * N + col] = f32_to_bf16(hv);
-                    }
-                }
-            }
-        }
+        col0 = cblk * (GWAVES * 16) + wave * 16;
+        const int64_t r = (int64_t)e * N + col0 + (lane & 15);
+        c.bp0 = B0 + r * K + (lane >> 4) * 8;
+        c.bp1 = B1 + r * K + (lane >> 4) * 8;
     } else {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = wrow0 + rb * 16 + 4 * (lane >> 4) + q;
-                if (m < te.row_count) {
-                    const int64_t p = sorted_pairs[te.row_begin + m];
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        const int col = n0 + wn * CB * 16 + cb * 16 + (lane & 15);
-                        C[p * N + col] = f32_to_bf16(acc[rb][cb][q]);
-                    }
-                }
-            }
-        }
+        col0 = cblk * (GWAVES * 32) + wave * 32;
+        const int64_t r = (int64_t)e * N + col0 + (lane & 15);
+        c.bp0 = B0 + r * K + (lane >> 4) * 8;
+        c.bp1 = c.bp0 + (int64_t)16 * K;
     }
+    c.ccol = col0 + (lane & 15);
+    c.A = A;
+    c.K = K;
+    c.top_k = top_k;
+
+    // row-count variants; small tiles are load-latency bound and keep 7 steps in flight
+    const int nrb = (te.row_count + 15) >> 4;
+    const bool deep = (c.nk & 7) == 0;
+    if (nrb > 16)
+        tile_body<GATED, 18, 4>(c, lds);
+    else if (nrb > 12)
+        tile_body<GATED, 16, 4>(c, lds);
+    else if (nrb > 8)
+        tile_body<GATED, 12, 4>(c, lds);
+    else if (nrb > 4)
+        tile_body<GATED, 8, 4>(c, lds);
+    else if (nrb > 2)
+        tile_body<GATED, 4, 4>(c, lds);
+    else if (nrb > 1)
+        deep ? tile_body<GATED, 2, 8>(c, lds) : tile_body<GATED, 2, 4>(c, lds);
+    else
+        deep ? tile_body<GATED, 1, 8>(c, lds) : tile_body<GATED, 1, 4>(c, lds);
 }
 
 int gemm_tile_rows(int64_t P, int E, bool bf16) {
-    if (!bf16) return 1 << 30;  // the fp32 path does not use tiles
-    const int64_t avg = E > 0 ? P / E : 0;
-    if (avg >= 64) return 128;
-    if (avg >= 16) return 32;
-    return 16;
+    (void)P;
+    (void)E;
+    return bf16 ? GROWS : (1 << 30);  // the fp32 path does not use tiles
 }
 
-template <int BM, int WM, bool GATED>
+template <bool GATED>
 static void launch_gemm(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int K, int N, int top_k,
                         const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                         int64_t max_tile_count, uint16_t* C, hipStream_t s) {
-    const int nout = GATED ? GBN / 2 : GBN;
-    const int ncb = N / nout;
-    const int64_t blocks = max_tile_count * ncb;
-    moe_gemm_bf16_kernel<BM, WM, GATED><<<(unsigned)blocks, GTHREADS, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs,
-                                                                             tiles, num_tiles, ncb, C);
+    const int ncols = GATED ? GWAVES * 16 : GWAVES * 32;
+    const int ncb = N / ncols;
+    const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
+    moe_gemm_bf16_kernel<GATED><<<(unsigned)blocks, GTHREADS, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs, tiles,
+                                                                     num_tiles, ncb, C);
 }
 
 hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int H, int I, int top_k,
                           const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                           int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
-    if (!bf16 || max_tile_count <= 0) return hipErrorInvalidValue;
-    auto A = (const uint16_t*)act;
-    auto g = (const uint16_t*)w_gate;
-    auto u = (const uint16_t*)w_up;
-    auto o = (uint16_t*)h;
-    if (tile_rows == 128)
-        launch_gemm<128, 2, true>(A, g, u, H, I, top_k, sorted_pairs, tiles, num_tiles, max_tile_count, o, s);
-    else if (tile_rows == 32)
-        launch_gemm<32, 2, true>(A, g, u, H, I, top_k, sorted_pairs, tiles, num_tiles, max_tile_count, o, s);
-    else if (tile_rows == 16)
-        launch_gemm<16, 1, true>(A, g, u, H, I, top_k, sorted_pairs, tiles, num_tiles, max_tile_count, o, s);
-    else
-        return hipErrorInvalidValue;
+    if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
+    launch_gemm<true>((const uint16_t*)act, (const uint16_t*)w_gate, (const uint16_t*)w_up, H, I, top_k, sorted_pairs,
+                      tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
     return hipGetLastError();
 }
 
 hipError_t launch_down(const void* h, bool bf16, const void* w_down, int H, int I, const int32_t* sorted_pairs,
                        const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, int tile_rows,
                        void* y_pair, hipStream_t s) {
-    if (!bf16 || max_tile_count <= 0) return hipErrorInvalidValue;
-    auto A = (const uint16_t*)h;
-    auto w = (const uint16_t*)w_down;
-    auto o = (uint16_t*)y_pair;
-    if (tile_rows == 128)
-        launch_gemm<128, 2, false>(A, w, nullptr, I, H, 0, sorted_pairs, tiles, num_tiles, max_tile_count, o, s);
-    else if (tile_rows == 32)
-        launch_gemm<32, 2, false>(A, w, nullptr, I, H, 0, sorted_pairs, tiles, num_tiles, max_tile_count, o, s);
-    else if (tile_rows == 16)
-        launch_gemm<16, 1, false>(A, w, nullptr, I, H, 0, sorted_pairs, tiles, num_tiles, max_tile_count, o, s);
-    else
-        return hipErrorInvalidValue;
+    if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
+    launch_gemm<false>((const uint16_t*)h, (const uint16_t*)w_down, nullptr, I, H, 0, sorted_pairs, tiles, num_tiles,
+                       max_tile_count, (uint16_t*)y_pair, s);
     return hipGetLastError();
 }
 

@@ -56,15 +56,19 @@ def test_workspace_size_rejects_invalid_shapes(bad):
 
 
 def test_unsupported_shapes():
-    for bad in (dict(H=5000), dict(I=2500)):
+    for bad in (dict(H=5000), dict(I=2500), dict(H=384), dict(I=192)):
         with pytest.raises(bm.BeamError) as ei:
             bm.workspace_size(_beam(**bad), bm.OP_FORWARD)
         assert ei.value.status == bm.BEAM_ERR_UNSUPPORTED
     with pytest.raises(bm.BeamError) as ei:
         bm.workspace_size(_beam(dtype="f32"), bm.OP_FORWARD_SUBLAYER)
     assert ei.value.status == bm.BEAM_ERR_UNSUPPORTED
-    # the fp32 path takes any H, I
+    # the fp32 path takes any H, I; routing alone only needs H % 32 in bf16
     assert bm.workspace_size(_beam(H=100, I=30, dtype="f32"), bm.OP_FORWARD) > 0
+    assert bm.workspace_size(_beam(H=96, I=30), bm.OP_ROUTE) > 0
+    with pytest.raises(bm.BeamError):
+        bm.workspace_size(_beam(H=80), bm.OP_ROUTE)
+    assert bm.workspace_size(_beam(H=80, I=30), bm.OP_PERMUTE) > 0
 
 
 def test_workspace_sizes():
