@@ -57,18 +57,30 @@ struct TileCtx {
     const uint16_t* bp0;  // this lane's first weight row (k offset applied)
     const uint16_t* bp1;  // second weight row block (up rows, or the next 16 down rows)
     int K, nk, top_k;     // reduction length, its 32-wide steps, routes per token
+    bool gather;          // activation rows come from token rows via sorted_pairs
     int row_begin, row_count, ccol, N;
     const int32_t* sorted_pairs;
     uint16_t* C;
 };
 
-// Main loop and epilogue for tiles of at most NRB 16-row blocks, with global loads
-// RING - 1 steps ahead.  Every load and store is unconditional (clamped addresses), so
-// the steady state has no branches and the compiler's memory-counter waits stay exact.
-// Only the NRB*16 activation rows the variant reads are loaded: thread t stages chunk
-// (t + 512 i) mod (NRB*64), so small tiles reload (cached) chunks instead of branching.
+// Activation source row of tile row `row` (rows past the tile read row 0; their results
+// are never stored).
+__device__ __forceinline__ const uint16_t* act_row(const TileCtx& c, int row) {
+    const int src = row < c.row_count ? row : 0;
+    const int64_t r = c.gather ? (int64_t)(c.sorted_pairs[c.row_begin + src] / c.top_k) : (int64_t)(c.row_begin + src);
+    return c.A + r * c.K;
+}
+
+// Main loop for tiles of at most NRB 16-row blocks (NRB >= 4).  Activations go
+// through an LDS double buffer: one register set stages step kt+2 while step kt+1 is
+// written to LDS and step kt is multiplied; weights stream RING-1 steps ahead.  Within
+// a step the loads are issued activations first, then weights, so waiting for the
+// staged activations never waits for the newest weight loads.  Every load and store is
+// unconditional (clamped addresses): the steady state has no branches and the
+// compiler's memory-counter waits stay exact.  Thread t stages chunk (t + 512 i) mod
+// (NRB*64), so smaller variants reload cached chunks instead of branching.
 template <bool GATED, int NRB, int RING>
-__device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
+__device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROWS * GKS], f32x4 (&acc)[NRB][2]) {
     constexpr int ACH = NRB * 64;                          // 16-byte activation chunks per step
     constexpr int AL = (ACH + GTHREADS - 1) / GTHREADS;    // activation loads per thread per step
     const int lane = threadIdx.x & 63;
@@ -79,66 +91,198 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     for (int i = 0; i < AL; ++i) {
         const int q = (tid + i * GTHREADS) % ACH;
         const int row = q >> 2, ch = q & 3;
-        const int src = row < c.row_count ? row : 0;  // rows past the tile read row 0 (never stored)
-        const int64_t arow = GATED ? (int64_t)(c.sorted_pairs[c.row_begin + src] / c.top_k)
-                                   : (int64_t)(c.row_begin + src);
-        ap[i] = c.A + arow * c.K + ch * 8;
+        ap[i] = act_row(c, row) + ch * 8;
         alds[i] = a_off(row, ch);
     }
 
-    u32x4 ra[RING][AL], rb[RING][2];
-    f32x4 acc[NRB][2];
-#pragma unroll
-    for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+    u32x4 sa[AL], rb[RING][2];
     const int nk = c.nk;
-    auto load = [&](int kstep, int set) {
-        const int k0 = (kstep < nk ? kstep : nk - 1) * GKS;  // past the end: reload the last step
+    auto clampk = [&](int kstep) { return (kstep < nk ? kstep : nk - 1) * GKS; };
+    auto load_a = [&](int kstep) {
+        const int k0 = clampk(kstep);
 #pragma unroll
-        for (int i = 0; i < AL; ++i) ra[set][i] = *(const u32x4*)(ap[i] + k0);
+        for (int i = 0; i < AL; ++i) sa[i] = *(const u32x4*)(ap[i] + k0);
+    };
+    auto load_b = [&](int kstep, int set) {
+        const int k0 = clampk(kstep);
         rb[set][0] = *(const u32x4*)(c.bp0 + k0);
         rb[set][1] = *(const u32x4*)(c.bp1 + k0);
     };
-    auto store_a = [&](int set, int buf) {
+    auto store_a = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) *(u32x4*)(&lds[buf][alds[i]]) = ra[set][i];
+        for (int i = 0; i < AL; ++i) *(u32x4*)(&lds[buf][alds[i]]) = sa[i];
     };
     const int rd_row = lane & 15, rd_ch = lane >> 4;
+    // fragment reads run LOOKAHEAD row blocks ahead of the MFMAs that use them
+    constexpr int LOOKAHEAD = NRB < 4 ? NRB : 4;
     auto compute = [&](int set, int buf) {
         const bf16x8 b0 = __builtin_bit_cast(bf16x8, rb[set][0]);
         const bf16x8 b1 = __builtin_bit_cast(bf16x8, rb[set][1]);
+        bf16x8 a[NRB];
+#pragma unroll
+        for (int r = 0; r < LOOKAHEAD; ++r) a[r] = *(const bf16x8*)(&lds[buf][a_off(r * 16 + rd_row, rd_ch)]);
+        __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
 #pragma unroll
         for (int r = 0; r < NRB; ++r) {
-            const bf16x8 a = *(const bf16x8*)(&lds[buf][a_off(r * 16 + rd_row, rd_ch)]);
-            acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[r][0], 0, 0, 0);
-            acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[r][1], 0, 0, 0);
+            if (r + LOOKAHEAD < NRB) {
+                a[r + LOOKAHEAD] = *(const bf16x8*)(&lds[buf][a_off((r + LOOKAHEAD) * 16 + rd_row, rd_ch)]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b0, acc[r][0], 0, 0, 0);
+            acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b1, acc[r][1], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
     };
     // one K step; `j` (= kt % RING) is a compile-time constant in the unrolled loop
     auto step = [&](int kt, auto jc) {
         constexpr int j = decltype(jc)::value;
-        load(kt + RING - 1, (j + RING - 1) % RING);
+        // the scheduling barriers keep this issue order (the compiler would otherwise
+        // sink the activation loads behind the weight loads and wait on both)
+        store_a((j + 1) & 1);                       // activations of step kt+1
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(kt + RING - 1, (j + RING - 1) % RING);
+        __builtin_amdgcn_sched_barrier(0);
         compute(j, j & 1);
-        store_a((j + 1) % RING, (j + 1) & 1);
         lds_barrier();
     };
 
+    // prologue in the steady-state issue order (activations, then weights), so the loop
+    // head sees the same outstanding loads from either path
+    load_a(0);
+    store_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < RING - 1; ++s) load(s, s);
-    store_a(0, 0);
+    for (int s = 0; s < RING - 1; ++s) {
+        load_b(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     lds_barrier();
     for (int kt = 0; kt < nk; kt += RING) {  // nk is a multiple of RING
         step(kt, std::integral_constant<int, 0>());
         step(kt + 1, std::integral_constant<int, 1>());
         step(kt + 2, std::integral_constant<int, 2>());
         step(kt + 3, std::integral_constant<int, 3>());
-        if constexpr (RING == 8) {
-            step(kt + 4, std::integral_constant<int, 4>());
-            step(kt + 5, std::integral_constant<int, 5>());
-            step(kt + 6, std::integral_constant<int, 6>());
-            step(kt + 7, std::integral_constant<int, 7>());
-        }
     }
+}
+
+// Main loop for tiles of at most NRB <= 2 row blocks (decode-sized), where the weight
+// stream is the whole cost.  K advances 64 per step.  Each lane loads, per 16-row weight
+// block, the 16-byte chunks 2*(lane>>4) and 2*(lane>>4)+1 of a 128-byte window; the two
+// MFMAs of a step take the first and the second chunk (the activation operand uses the
+// same k order), so each pair of back-to-back loads reads whole 128-byte lines of 16
+// rows.  Weights run RING-1 steps ahead.  Activations are staged through LDS in chunks
+// of SKC columns for all rows of the tile (one barrier per chunk); the next chunk's
+// global loads are issued a whole chunk ahead.
+constexpr int SKC = 512;            // activation columns per LDS chunk
+constexpr int SKS = SKC / 64;       // steps per chunk
+
+// LDS element offset of 16-byte chunk `ch` (0..SKC/8-1) of activation row `row`
+__device__ __forceinline__ int s_off(int row, int ch) { return row * SKC + ((ch ^ (row & 15)) << 3); }
+
+template <bool GATED, int NRB, int RING>
+__device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
+    constexpr int ROWS = NRB * 16;
+    constexpr int ACH = ROWS * SKC / 8;          // 16-byte chunks per activation chunk
+    constexpr int AL = ACH / GTHREADS;           // per thread
+    static_assert(AL * GTHREADS == ACH, "activation chunk split");
+    const int lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int nk = c.K / 64;                     // steps
+    const int nchunk = c.K / SKC;
+    // activation staging of this thread
+    const uint16_t* ap[AL];
+    int alds[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int q = tid + i * GTHREADS;
+        const int row = q / (SKC / 8), ch = q % (SKC / 8);
+        ap[i] = act_row(c, row) + ch * 8;
+        alds[i] = s_off(row, ch);
+    }
+    u32x4 sa[AL];
+    auto load_a = [&](int chunk) {
+        const int k0 = (chunk < nchunk ? chunk : nchunk - 1) * SKC;
+#pragma unroll
+        for (int i = 0; i < AL; ++i) sa[i] = *(const u32x4*)(ap[i] + k0);
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) *(u32x4*)(lds + buf * (ROWS * SKC) + alds[i]) = sa[i];
+    };
+    // weights: lane's two chunks of each 128-byte window of its two 16-row blocks
+    const uint16_t* b0 = c.bp0 - (lane >> 4) * 8 + (lane >> 4) * 16;  // chunk 2*(lane>>4)
+    const uint16_t* b1 = c.bp1 - (lane >> 4) * 8 + (lane >> 4) * 16;
+    u32x4 rb[RING][4];
+    auto load_b = [&](int kstep, int set) {
+        const int k0 = (kstep < nk ? kstep : nk - 1) * 64;
+        rb[set][0] = *(const u32x4*)(b0 + k0);
+        rb[set][1] = *(const u32x4*)(b0 + k0 + 8);
+        rb[set][2] = *(const u32x4*)(b1 + k0);
+        rb[set][3] = *(const u32x4*)(b1 + k0 + 8);
+    };
+    auto compute = [&](int kstep, int set, int buf) {
+        const int w = (kstep % SKS) * 8;  // 16-byte chunk of the window inside the LDS chunk
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bf16x8 g = __builtin_bit_cast(bf16x8, rb[set][h]);
+            const bf16x8 u = __builtin_bit_cast(bf16x8, rb[set][2 + h]);
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) {
+                const bf16x8 a = *(const bf16x8*)(lds + buf * (ROWS * SKC) +
+                                                  s_off(r * 16 + (lane & 15), w + 2 * (lane >> 4) + h));
+                acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g, acc[r][0], 0, 0, 0);
+                acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u, acc[r][1], 0, 0, 0);
+            }
+        }
+    };
+    // prologue: chunk 0 into LDS, chunk 1 in flight, weights RING-1 steps ahead
+    load_a(0);
+    store_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < RING - 1; ++s) {
+        load_b(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+    for (int ck = 0; ck < nchunk; ++ck) {
+        const int buf = ck & 1;
+#pragma unroll
+        for (int j = 0; j < SKS; ++j) {  // SKS is a multiple of RING: ring slots are static
+            const int kt = ck * SKS + j;
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(kt + RING - 1, (j + RING - 1) % RING);
+            compute(kt, j % RING, buf);
+        }
+        // next chunk: stage it into the other buffer (read by no wave since the last
+        // barrier), then put the one after it in flight
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(ck + 2);
+        lds_barrier();
+    }
+}
+
+// Runs one tile: main loop variant, then the epilogue.
+template <bool GATED, int NRB, int RING>
+__device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
+    const int lane = threadIdx.x & 63;
+    f32x4 acc[NRB][2];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NRB <= 2) {
+        if (c.K % SKC == 0)
+            tile_body_stream<GATED, NRB, RING>(c, &lds[0][0], acc);
+        else
+            tile_body<GATED, NRB, RING>(c, lds, acc);
+    } else
+        tile_body<GATED, NRB, RING>(c, lds, acc);
 
     // ---- epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15) ----
 #pragma unroll
@@ -168,7 +312,9 @@ __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t*
                                                                  const TileEntry* __restrict__ tiles,
                                                                  const int32_t* __restrict__ num_tiles,
                                                                  int n_col_blocks, uint16_t* __restrict__ C) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][GROWS * GKS];
+    constexpr int LDS_ELEMS = 2 * GROWS * GKS > 2 * 32 * SKC ? 2 * GROWS * GKS : 2 * 32 * SKC;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_raw[LDS_ELEMS];
+    auto lds = reinterpret_cast<uint16_t (*)[GROWS * GKS]>(lds_raw);
 
     // XCD-aware order: blocks are dealt round-robin to the 8 XCDs, so give each XCD a
     // contiguous run of work items (the column blocks of one tile share its activation
@@ -212,24 +358,25 @@ __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t*
     c.A = A;
     c.K = K;
     c.top_k = top_k;
+    c.gather = GATED;
 
     // row-count variants; small tiles are load-latency bound and keep 7 steps in flight
     const int nrb = (te.row_count + 15) >> 4;
-    const bool deep = (c.nk & 7) == 0;
+
     if (nrb > 16)
-        tile_body<GATED, 18, 4>(c, lds);
+        run_tile<GATED, 18, 4>(c, lds);
     else if (nrb > 12)
-        tile_body<GATED, 16, 4>(c, lds);
+        run_tile<GATED, 16, 4>(c, lds);
     else if (nrb > 8)
-        tile_body<GATED, 12, 4>(c, lds);
+        run_tile<GATED, 12, 4>(c, lds);
     else if (nrb > 4)
-        tile_body<GATED, 8, 4>(c, lds);
+        run_tile<GATED, 8, 4>(c, lds);
     else if (nrb > 2)
-        tile_body<GATED, 4, 4>(c, lds);
+        run_tile<GATED, 4, 4>(c, lds);
     else if (nrb > 1)
-        deep ? tile_body<GATED, 2, 8>(c, lds) : tile_body<GATED, 2, 4>(c, lds);
+        run_tile<GATED, 2, 4>(c, lds);
     else
-        deep ? tile_body<GATED, 1, 8>(c, lds) : tile_body<GATED, 1, 4>(c, lds);
+        run_tile<GATED, 1, 4>(c, lds);
 }
 
 int gemm_tile_rows(int64_t P, int E, bool bf16) {
