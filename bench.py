@@ -198,7 +198,7 @@ def main():
     ap.add_argument("--workload", default="prefill_t8192",
                     choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768"])
     ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
-    ap.add_argument("--cpu-tokens", type=int, default=384, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB")
     args = ap.parse_args()

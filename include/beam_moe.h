@@ -61,7 +61,7 @@ typedef enum beam_dtype { BEAM_F32 = 0, BEAM_BF16 = 1 } beam_dtype;
  * E % n_group == 0; E / n_group <= 1024; 1 <= n_group <= 64;
  * 1 <= topk_group <= n_group; 1 <= top_k <= min(32, topk_group * E / n_group);
  * H, I >= 1.  With BEAM_BF16, beam_moe_forward needs H % 256 == 0 and
- * I % 128 == 0, and beam_moe_route needs H % 32 == 0 (else BEAM_ERR_UNSUPPORTED).
+ * I % 128 == 0, and beam_moe_route needs H % 128 == 0 (else BEAM_ERR_UNSUPPORTED).
  * Beam: H = 5120, E = 256, I = 2560, n_group = 8, topk_group = 4, top_k = 8,
  * routed_scaling = 2.5.
  */
@@ -91,7 +91,7 @@ typedef struct beam_sublayer {
 
 /* what a workspace is for */
 typedef enum beam_op {
-    BEAM_OP_ROUTE = 0,            /* beam_moe_route with logits_out == NULL */
+    BEAM_OP_ROUTE = 0,            /* beam_moe_route */
     BEAM_OP_PERMUTE = 1,          /* beam_moe_permute */
     BEAM_OP_FORWARD = 2,          /* beam_moe_forward without sublayer */
     BEAM_OP_FORWARD_SUBLAYER = 3  /* beam_moe_forward with sublayer */
@@ -134,12 +134,13 @@ beam_status beam_moe_rmsnorm(const beam_moe_shape* shape, const void* x, const f
  *   topk_idx [T,top_k] int32 out: chosen experts, descending s', ties -> lower id
  *   topk_w   [T,top_k] fp32 out: routed_scaling * s / sum(s) of the chosen
  *   logits_out [T,E] fp32 out, optional (the router logits before the sigmoid)
- *   ws       scratch of beam_moe_workspace_size(BEAM_OP_ROUTE) bytes; may be NULL
- *            (ws_bytes 0) when logits_out is given.
+ *   ws       scratch of beam_moe_workspace_size(BEAM_OP_ROUTE) bytes (fp64 partial
+ *            logits; several H ranges are reduced by different work-groups when T
+ *            is small)
  * Logits are accumulated from exact bf16 x bf16 partial products: each 32-term
- * block is summed on the matrix cores in fp32, the blocks are summed in fp64, and
- * the logit is rounded once to fp32; s, s', group scores and all comparisons are
- * fp32.
+ * block is summed on the matrix cores in fp32, the blocks and H ranges are summed in
+ * fp64 in a fixed order, and the logit is rounded once to fp32; s, s', group scores
+ * and all comparisons are fp32.
  */
 beam_status beam_moe_route(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
                            int32_t* topk_idx, float* topk_w, float* logits_out, void* ws, size_t ws_bytes,

@@ -27,18 +27,19 @@ bool shape_valid(const beam_moe_shape* s) {
     return true;
 }
 
-// bf16 kernels: the router sweeps H in 32-wide MFMA steps; the expert GEMMs sweep K in
+// bf16 kernels: the router sweeps H in groups of 4 32-wide MFMA steps; the expert GEMMs sweep K in
 // 128-wide unrolled groups and cover N in 128 (gate/up) or 256 (down) column blocks.
-bool route_supported(const beam_moe_shape* s) { return s->dtype != BEAM_BF16 || s->H % 32 == 0; }
+bool route_supported(const beam_moe_shape* s) { return s->dtype != BEAM_BF16 || s->H % 128 == 0; }
 bool shape_supported(const beam_moe_shape* s) {
     if (s->dtype == BEAM_BF16) return s->H % 256 == 0 && s->I % 128 == 0;
     return true;
 }
 
 struct Layout {
-    size_t logits = 0, idx = 0, w = 0, u = 0, scratch = 0, offsets = 0, sorted = 0, pos = 0, ntiles = 0, tiles = 0,
+    size_t part = 0, idx = 0, w = 0, u = 0, scratch = 0, offsets = 0, sorted = 0, pos = 0, ntiles = 0, tiles = 0,
            h = 0, ypair = 0, total = 0;
     int tile_rows = 0;
+    int nsplit = 1;  // router reduction splits
     int64_t max_tiles = 0;
 };
 
@@ -52,15 +53,16 @@ Layout make_layout(const beam_moe_shape* s, int op) {
     };
     const int64_t T = s->T, P = T * s->top_k;
     const size_t elt = s->dtype == BEAM_BF16 ? 2 : 4;
+    L.nsplit = s->dtype == BEAM_BF16 ? beam::router_splits(T, s->H, s->E) : 1;
     if (op == BEAM_OP_ROUTE) {
-        L.logits = take((size_t)T * s->E * 4);
+        L.part = take((size_t)L.nsplit * T * s->E * 8);
     } else if (op == BEAM_OP_PERMUTE) {
         L.scratch = take(beam::permute_scratch_words(P, s->E) * 4);
     } else {
         const bool bf16 = s->dtype == BEAM_BF16;
         L.tile_rows = beam::gemm_tile_rows(P, s->E, bf16);
         L.max_tiles = bf16 ? beam::max_tiles(P, s->E, L.tile_rows) : 0;
-        L.logits = take((size_t)T * s->E * 4);
+        L.part = take((size_t)L.nsplit * T * s->E * 8);
         L.idx = take((size_t)P * 4);
         L.w = take((size_t)P * 4);
         if (op == BEAM_OP_FORWARD_SUBLAYER) L.u = take((size_t)T * s->H * 2);
@@ -131,18 +133,16 @@ beam_status beam_moe_route(const beam_moe_shape* shape, const void* x, const flo
     if (!route_supported(shape)) return BEAM_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_router)) return BEAM_ERR_INVALID_ARG;
     if (shape->T == 0) return BEAM_OK;
-    float* logits = logits_out;
-    if (!logits) {
-        const Layout L = make_layout(shape, BEAM_OP_ROUTE);
-        if (!ws || ws_bytes < L.total) return BEAM_ERR_WORKSPACE;
-        logits = at<float>(ws, L.logits);
-    }
+    const Layout L = make_layout(shape, BEAM_OP_ROUTE);
+    if (!ws || ws_bytes < L.total) return BEAM_ERR_WORKSPACE;
+    double* part = at<double>(ws, L.part);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = shape->dtype == BEAM_BF16;
-    hipError_t e = beam::launch_router_logits(x, bf16, w_router, shape->T, shape->H, shape->E, logits, s);
+    hipError_t e = beam::launch_router_logits(x, bf16, w_router, shape->T, shape->H, shape->E, L.nsplit, part, s);
     if (e != hipSuccess) return BEAM_ERR_HIP;
-    return hip_status(beam::launch_router_select(logits, bias, shape->T, shape->E, shape->n_group, shape->topk_group,
-                                                 shape->top_k, shape->routed_scaling, topk_idx, topk_w, s));
+    return hip_status(beam::launch_router_select(part, L.nsplit, bias, shape->T, shape->E, shape->n_group,
+                                                 shape->topk_group, shape->top_k, shape->routed_scaling, topk_idx,
+                                                 topk_w, logits_out, s));
 }
 
 beam_status beam_moe_permute(const beam_moe_shape* shape, const int32_t* topk_idx, int32_t* offsets,
@@ -205,10 +205,10 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
         act = u;
     }
     BEAM_TRY(mark(BEAM_STAGE_ROUTER_LOGITS));
-    BEAM_TRY(beam::launch_router_logits(act, bf16, w_router, T, H, E, at<float>(ws, L.logits), s));
+    BEAM_TRY(beam::launch_router_logits(act, bf16, w_router, T, H, E, L.nsplit, at<double>(ws, L.part), s));
     BEAM_TRY(mark(BEAM_STAGE_ROUTER_SELECT));
-    BEAM_TRY(beam::launch_router_select(at<float>(ws, L.logits), bias, T, E, shape->n_group, shape->topk_group, K,
-                                        shape->routed_scaling, idx, w, s));
+    BEAM_TRY(beam::launch_router_select(at<double>(ws, L.part), L.nsplit, bias, T, E, shape->n_group,
+                                        shape->topk_group, K, shape->routed_scaling, idx, w, nullptr, s));
     BEAM_TRY(mark(BEAM_STAGE_PERMUTE));
     BEAM_TRY(beam::launch_permute(idx, P, E, at<int32_t>(ws, L.scratch), at<int32_t>(ws, L.offsets), sorted,
                                   at<int32_t>(ws, L.pos), bf16 ? tiles : nullptr, bf16 ? ntiles : nullptr,

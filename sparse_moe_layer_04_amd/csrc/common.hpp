@@ -40,12 +40,19 @@ struct TileEntry {
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, int64_t T, int H, uint16_t* u,
                           hipStream_t s);
 
-// logits [T,E] fp32 from activations (bf16 or fp32) and the fp32 router matrix
-hipError_t launch_router_logits(const void* x, bool bf16, const float* w_router, int64_t T, int H, int E,
-                                float* logits, hipStream_t s);
+// number of H ranges the bf16 router splits its reduction into (1 for fp32)
+int router_splits(int64_t T, int H, int E);
 
-hipError_t launch_router_select(const float* logits, const float* bias, int64_t T, int E, int n_group,
-                                int topk_group, int top_k, float rho, int32_t* idx, float* w, hipStream_t s);
+// fp64 partial logits part[nsplit][T][E] from activations (bf16 or fp32; fp32 needs
+// nsplit == 1) and the fp32 router matrix
+hipError_t launch_router_logits(const void* x, bool bf16, const float* w_router, int64_t T, int H, int E,
+                                int nsplit, double* part, hipStream_t s);
+
+// sums the partials in split order, rounds the logits to fp32 (written to logits_out
+// when non-null) and selects the experts
+hipError_t launch_router_select(const double* part, int nsplit, const float* bias, int64_t T, int E, int n_group,
+                                int topk_group, int top_k, float rho, int32_t* idx, float* w, float* logits_out,
+                                hipStream_t s);
 
 // scratch words the permutation needs for P pairs and E experts
 size_t permute_scratch_words(int64_t P, int E);

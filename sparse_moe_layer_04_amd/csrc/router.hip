@@ -17,14 +17,19 @@ namespace beam {
 // ---------------------------------------------------------------------------------
 // Logits for bf16 activations.  Each fp32 router weight is split exactly into three
 // bf16 parts (hi + mid + lo, by truncation), so every MFMA product x*part is exact
-// in fp32.  MFMA sums each 32-term block (lo, mid, then hi parts) in fp32; the
-// blocks are summed in fp64 and the logit is rounded once to fp32.
+// in fp32.  MFMA sums each 32-term block (lo, mid, then hi parts) in fp32; the blocks
+// are summed in fp64.  The H columns may be split into `nsplit` ranges handled by
+// different work-groups (small T needs the parallelism); each writes an fp64 partial
+// and the selection kernel adds the partials in split order before rounding the logit
+// once to fp32, so the result does not depend on scheduling.
 //
 // Work-group: 4 waves, 32 tokens x 128 experts; wave w owns experts [32w, 32w+32).
-// Operands are read straight from global memory (the matrix is L2-resident).
+// Operands are read straight from global memory (the matrix is cache-resident), with
+// the loads of the next RL_RING-1 steps in flight.
 // ---------------------------------------------------------------------------------
 constexpr int RL_TOK = 32;
 constexpr int RL_EXP = 128;
+constexpr int RL_RING = 4;
 
 __device__ __forceinline__ void split3(float w, float& hi, float& mid, float& lo) {
     hi = __uint_as_float(__float_as_uint(w) & 0xFFFF0000u);
@@ -38,53 +43,57 @@ __device__ __forceinline__ __bf16 as_bf16_trunc(float f) {
     return __builtin_bit_cast(__bf16, b);
 }
 
+// x [T,H] bf16, wr [E,H] fp32 -> part [nsplit][T][E] fp64 (split s covers columns
+// [s*klen, (s+1)*klen), klen a multiple of 32 * RL_RING).
 __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr, int64_t T, int H,
-                                                                 int E, float* __restrict__ logits) {
+                                                                 int E, int klen, double* __restrict__ part) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * RL_TOK;
     const int e0 = blockIdx.y * RL_EXP + wave * 32;
+    const int split = blockIdx.z;
     if (e0 >= E) return;  // whole wave idle (uniform)
 
-    const int kq = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide k step
+    const int kq = (lane >> 4) * 8 + split * klen;  // k offset of this lane
     const uint16_t* arow[2];
-    bool aval[2];
-    for (int rb = 0; rb < 2; ++rb) {
-        int64_t t = t0 + rb * 16 + (lane & 15);
-        aval[rb] = t < T;
-        arow[rb] = x + (aval[rb] ? t : 0) * (int64_t)H + kq;
-    }
     const float* brow[2];
-    bool bval[2];
+    for (int rb = 0; rb < 2; ++rb) {
+        const int64_t t = t0 + rb * 16 + (lane & 15);
+        arow[rb] = x + (t < T ? t : T - 1) * (int64_t)H + kq;  // rows past T repeat row T-1
+    }
     for (int cb = 0; cb < 2; ++cb) {
-        int e = e0 + cb * 16 + (lane & 15);
-        bval[cb] = e < E;
-        brow[cb] = wr + (int64_t)(bval[cb] ? e : 0) * H + kq;
+        const int e = e0 + cb * 16 + (lane & 15);
+        brow[cb] = wr + (int64_t)(e < E ? e : E - 1) * H + kq;
     }
 
     f32x4 acc[2][2];
     double acc64[2][2][4];
     for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j) {
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j)
             for (int q = 0; q < 4; ++q) acc64[i][j][q] = 0.0;
-        }
 
-    const int nks = H / 32;
-    for (int ks = 0; ks < nks; ++ks) {
-        const int k0 = ks * 32;
-        bf16x8 a[2];
-        for (int rb = 0; rb < 2; ++rb) {
-            u32x4 v = aval[rb] ? *(const u32x4*)(arow[rb] + k0) : u32x4{0u, 0u, 0u, 0u};
-            a[rb] = __builtin_bit_cast(bf16x8, v);
-        }
+    u32x4 ra[RL_RING][2];
+    f32x4 rw[RL_RING][2][2];
+    const int nks = klen / 32;
+    auto load = [&](int ks, int set) {
+        const int k0 = (ks < nks ? ks : nks - 1) * 32;
+        for (int rb = 0; rb < 2; ++rb) ra[set][rb] = *(const u32x4*)(arow[rb] + k0);
         for (int cb = 0; cb < 2; ++cb) {
-            f32x4 w0 = bval[cb] ? *(const f32x4*)(brow[cb] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 w1 = bval[cb] ? *(const f32x4*)(brow[cb] + k0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            rw[set][cb][0] = *(const f32x4*)(brow[cb] + k0);
+            rw[set][cb][1] = *(const f32x4*)(brow[cb] + k0 + 4);
+        }
+    };
+    auto step = [&](int ks, int set) {
+        load(ks + RL_RING - 1, (set + RL_RING - 1) % RL_RING);
+        for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 a[2];
+        for (int rb = 0; rb < 2; ++rb) a[rb] = __builtin_bit_cast(bf16x8, ra[set][rb]);
+        for (int cb = 0; cb < 2; ++cb) {
             bf16x8 bh, bm, bl;
             for (int q = 0; q < 8; ++q) {
-                float w = q < 4 ? w0[q] : w1[q - 4];
+                const float w = q < 4 ? rw[set][cb][0][q] : rw[set][cb][1][q - 4];
                 float hi, mid, lo;
                 split3(w, hi, mid, lo);
                 bh[q] = as_bf16_trunc(hi);
@@ -100,45 +109,60 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
         // fold each 32-term block into fp64: the matrix-core sum rounds once per
         // instruction, so short fp32 chains keep the logit error near one fp32 ulp
         for (int i = 0; i < 2; ++i)
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < 2; ++j)
                 for (int q = 0; q < 4; ++q) acc64[i][j][q] += (double)acc[i][j][q];
-                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+    };
+    for (int s = 0; s < RL_RING - 1; ++s) load(s, s);
+    for (int ks = 0; ks < nks; ks += RL_RING) {  // nks is a multiple of RL_RING
+        step(ks, 0);
+        step(ks + 1, 1);
+        step(ks + 2, 2);
+        step(ks + 3, 3);
     }
     // C layout of a 16x16 MFMA block: lane holds rows 4*(lane>>4)+q, column lane&15
+    double* out = part + (int64_t)split * T * E;
     for (int rb = 0; rb < 2; ++rb)
         for (int cb = 0; cb < 2; ++cb) {
-            int e = e0 + cb * 16 + (lane & 15);
+            const int e = e0 + cb * 16 + (lane & 15);
             for (int q = 0; q < 4; ++q) {
-                int64_t t = t0 + rb * 16 + 4 * (lane >> 4) + q;
-                if (t < T && e < E) logits[t * E + e] = (float)acc64[rb][cb][q];
+                const int64_t t = t0 + rb * 16 + 4 * (lane >> 4) + q;
+                if (t < T && e < E) out[t * E + e] = acc64[rb][cb][q];
             }
         }
 }
 
+int router_splits(int64_t T, int H, int E) {
+    const int64_t tiles = ((T + RL_TOK - 1) / RL_TOK) * ((E + RL_EXP - 1) / RL_EXP);
+    const int units = H / (32 * RL_RING);  // split granularity
+    int best = 1;
+    for (int d = 1; d <= units; ++d)
+        if (units % d == 0 && tiles * d <= 1024) best = d;
+    return best;
+}
+
 // fp32 activations: one thread per (token, expert), fp64 accumulation.
 __global__ void router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr, int64_t T, int H,
-                                         int E, float* __restrict__ logits) {
+                                         int E, double* __restrict__ part) {
     int64_t n = T * E;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         int64_t t = i / E;
         int e = (int)(i % E);
         double acc = 0.0;
         for (int h = 0; h < H; ++h) acc += (double)x[t * H + h] * (double)wr[(int64_t)e * H + h];
-        logits[i] = (float)acc;
+        part[i] = acc;
     }
 }
 
 hipError_t launch_router_logits(const void* x, bool bf16, const float* w_router, int64_t T, int H, int E,
-                                float* logits, hipStream_t s) {
+                                int nsplit, double* part, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (bf16) {
-        dim3 grid((unsigned)((T + RL_TOK - 1) / RL_TOK), (unsigned)((E + RL_EXP - 1) / RL_EXP));
-        router_logits_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, w_router, T, H, E, logits);
+        dim3 grid((unsigned)((T + RL_TOK - 1) / RL_TOK), (unsigned)((E + RL_EXP - 1) / RL_EXP), (unsigned)nsplit);
+        router_logits_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, w_router, T, H, E, H / nsplit, part);
     } else {
         int64_t n = T * E;
         unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-        router_logits_f32_kernel<<<blocks, 256, 0, s>>>((const float*)x, w_router, T, H, E, logits);
+        router_logits_f32_kernel<<<blocks, 256, 0, s>>>((const float*)x, w_router, T, H, E, part);
     }
     return hipGetLastError();
 }
@@ -158,12 +182,13 @@ __device__ __forceinline__ bool ranks_before(float va, int a, float vb, int b) {
     return va > vb || (va == vb && a < b);
 }
 
-__global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const float* __restrict__ logits,
+__global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const double* __restrict__ part, int nsplit,
                                                                        const float* __restrict__ bias, int64_t T,
                                                                        int E, int n_group, int topk_group,
                                                                        int top_k, float rho,
                                                                        int32_t* __restrict__ idx_out,
-                                                                       float* __restrict__ w_out) {
+                                                                       float* __restrict__ w_out,
+                                                                       float* __restrict__ logits_out) {
     __shared__ float s_sc[SEL_WAVES][SEL_MAX_E];
     __shared__ float s_sb[SEL_WAVES][SEL_MAX_E];
     __shared__ float s_gs[SEL_WAVES][SEL_MAX_G];
@@ -176,11 +201,41 @@ __global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const flo
     const int gsize = E / n_group;
 
     if (active) {
-        for (int e = lane; e < E; e += 64) {
-            float l = logits[t * E + e];
-            float sc = (float)(1.0 / (1.0 + exp(-(double)l)));
-            s_sc[wave][e] = sc;
-            s_sb[wave][e] = sc + bias[e];
+        // four experts per lane at a time, partials read four splits at a time, so that
+        // 16 loads are in flight; each logit still adds its partials in split order
+        for (int eb = lane; eb < E; eb += 256) {
+            double l64[4] = {0.0, 0.0, 0.0, 0.0};
+            int sp = 0;
+            for (; sp + 4 <= nsplit; sp += 4) {
+                double v[4][4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = eb + 64 * u < E ? eb + 64 * u : E - 1;
+                        v[a][u] = part[((int64_t)(sp + a) * T + t) * E + e];
+                    }
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) l64[u] += v[a][u];
+            }
+            for (; sp < nsplit; ++sp)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = eb + 64 * u < E ? eb + 64 * u : E - 1;
+                    l64[u] += part[((int64_t)sp * T + t) * E + e];
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = eb + 64 * u;
+                if (e >= E) break;
+                const float l = (float)l64[u];
+                if (logits_out) logits_out[t * E + e] = l;
+                float sc = (float)(1.0 / (1.0 + exp(-(double)l)));
+                s_sc[wave][e] = sc;
+                s_sb[wave][e] = sc + bias[e];
+            }
         }
     }
     __syncthreads();
@@ -251,12 +306,13 @@ __global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const flo
     }
 }
 
-hipError_t launch_router_select(const float* logits, const float* bias, int64_t T, int E, int n_group,
-                                int topk_group, int top_k, float rho, int32_t* idx, float* w, hipStream_t s) {
+hipError_t launch_router_select(const double* part, int nsplit, const float* bias, int64_t T, int E, int n_group,
+                                int topk_group, int top_k, float rho, int32_t* idx, float* w, float* logits_out,
+                                hipStream_t s) {
     if (T == 0) return hipSuccess;
     unsigned blocks = (unsigned)((T + SEL_WAVES - 1) / SEL_WAVES);
-    router_select_kernel<<<blocks, SEL_WAVES * 64, 0, s>>>(logits, bias, T, E, n_group, topk_group, top_k, rho, idx,
-                                                          w);
+    router_select_kernel<<<blocks, SEL_WAVES * 64, 0, s>>>(part, nsplit, bias, T, E, n_group, topk_group, top_k, rho,
+                                                          idx, w, logits_out);
     return hipGetLastError();
 }
 

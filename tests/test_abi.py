@@ -63,11 +63,11 @@ def test_unsupported_shapes():
     with pytest.raises(bm.BeamError) as ei:
         bm.workspace_size(_beam(dtype="f32"), bm.OP_FORWARD_SUBLAYER)
     assert ei.value.status == bm.BEAM_ERR_UNSUPPORTED
-    # the fp32 path takes any H, I; routing alone only needs H % 32 in bf16
+    # the fp32 path takes any H, I; routing alone only needs H % 128 in bf16
     assert bm.workspace_size(_beam(H=100, I=30, dtype="f32"), bm.OP_FORWARD) > 0
-    assert bm.workspace_size(_beam(H=96, I=30), bm.OP_ROUTE) > 0
+    assert bm.workspace_size(_beam(H=384, I=30), bm.OP_ROUTE) > 0
     with pytest.raises(bm.BeamError):
-        bm.workspace_size(_beam(H=80), bm.OP_ROUTE)
+        bm.workspace_size(_beam(H=96), bm.OP_ROUTE)
     assert bm.workspace_size(_beam(H=80, I=30), bm.OP_PERMUTE) > 0
 
 
@@ -117,10 +117,13 @@ def test_forward_validation_happens_before_launch():
 def test_route_permute_rmsnorm_validation():
     L = bm.lib()
     s = _beam(T=64)
-    # route: missing outputs; missing workspace without logits_out
+    # route: missing outputs; missing or short workspace (with or without logits_out)
     assert L.beam_moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == \
         bm.BEAM_ERR_INVALID_ARG
     assert L.beam_moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == \
+        bm.BEAM_ERR_WORKSPACE
+    need = bm.workspace_size(s, bm.OP_ROUTE)
+    assert L.beam_moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
         bm.BEAM_ERR_WORKSPACE
     s0 = _beam(T=0)
     assert L.beam_moe_route(ctypes.byref(s0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == bm.BEAM_OK

@@ -63,14 +63,14 @@ def test_route_logits_and_selection():
     idx = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device="cuda")
     logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
-    bm.route(shape, d.x, d.wr, d.bias, idx, w, logits_out=logits)
+    ws = torch.empty(bm.workspace_size(shape, bm.OP_ROUTE), dtype=torch.uint8, device="cuda")
+    bm.route(shape, d.x, d.wr, d.bias, idx, w, logits_out=logits, ws=ws)
     torch.cuda.synchronize()
     lerr = np.abs(host(logits).astype(np.float64) - ref.logits).max()
     print("max |logit - fp64 logit| = %.3e" % lerr)
     assert lerr <= 2e-6  # keeps every score within half the 1e-6 tie margin
     assert_routing_equal(host(idx), host(w), ref.idx, ref.w, cfg.rho)
-    # the workspace variant gives the same answer
-    ws = torch.empty(bm.workspace_size(shape, bm.OP_ROUTE), dtype=torch.uint8, device="cuda")
+    # without the logits output the answer is the same
     idx2 = torch.empty_like(idx)
     w2 = torch.empty_like(w)
     bm.route(shape, d.x, d.wr, d.bias, idx2, w2, ws=ws)
@@ -95,7 +95,8 @@ def test_route_hand_worked_fixture_on_gpu():
     idx = torch.empty((1, fx["top_k"]), dtype=torch.int32, device="cuda")
     w = torch.empty((1, fx["top_k"]), dtype=torch.float32, device="cuda")
     logits = torch.empty((1, fx["E"]), dtype=torch.float32, device="cuda")
-    bm.route(shape, dev(synth.f32_to_bf16(x)), dev(wr), dev(np.zeros(fx["E"], np.float32)), idx, w, logits)
+    ws = torch.empty(bm.workspace_size(shape, bm.OP_ROUTE), dtype=torch.uint8, device="cuda")
+    bm.route(shape, dev(synth.f32_to_bf16(x)), dev(wr), dev(np.zeros(fx["E"], np.float32)), idx, w, logits, ws)
     torch.cuda.synchronize()
     assert host(idx)[0].tolist() == fx["expected_idx"]
     np.testing.assert_allclose(host(w)[0], fx["expected_w"], rtol=1e-6)
