@@ -8,6 +8,7 @@ line is the 8192-token prefill layer; the same run also times the 64-token decod
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prefill_t8192]
   python bench.py --copy-calib 1024      # plain 1 GiB device copy (HBM counter calibration)
+  python bench.py --workload W --ingest-pmc FETCH.csv WRITE.csv CALIB_FETCH.csv CALIB_WRITE.csv 1024
 """
 from __future__ import annotations
 
@@ -67,19 +68,66 @@ def roofline(flops, nbytes, seconds, traffic=None):
             "traffic": traffic}
 
 
-def load_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter runs, or None when the kernel
-    source changed since they were taken."""
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` ("gate_up" or "down") from the committed counter runs,
+    or None when the kernel source changed since they were taken."""
     try:
         with open(TRAFFIC_JSON) as f:
             d = json.load(f)
         ent = d[workload]
         if ent.get("experts_hip_sha256_16") != kernel_source_hash():
             return None
-        return {"fetch_bytes": ent["fetch_bytes"], "write_bytes": ent["write_bytes"],
-                "bytes": ent["fetch_bytes"] + ent["write_bytes"], "source": os.path.relpath(TRAFFIC_JSON, ROOT)}
-    except (OSError, KeyError, ValueError):
+        k = ent[kernel]
+        return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+                "bytes": k["fetch_bytes"] + k["write_bytes"], "source": os.path.relpath(TRAFFIC_JSON, ROOT)}
+    except (OSError, KeyError, ValueError, TypeError):
         return None
+
+
+KERNEL_NAMES = {"gate_up": "moe_gemm_bf16_kernel<true>", "down": "moe_gemm_bf16_kernel<false>"}
+
+
+def _counter_means(path, counter):
+    """Mean value of `counter` per dispatch, keyed by kernel name, from a rocprofv3 --pmc csv."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def ingest_counters(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_mib):
+    """Record HBM traffic per launch of the expert GEMMs into profiles/traffic.json.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same counters read
+    for a plain device copy of calib_mib MiB (the largest kernel in the calibration runs)."""
+    n = calib_mib * 2 ** 20
+    cf = max(_counter_means(calib_fetch_csv, "FETCH_SIZE").values()) * 1024.0
+    cw = max(_counter_means(calib_write_csv, "WRITE_SIZE").values()) * 1024.0
+    f_fetch, f_write = n / cf, n / cw
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    ent = {"experts_hip_sha256_16": kernel_source_hash(),
+           "calibration": {"copy_bytes": n, "fetch_factor": f_fetch, "write_factor": f_write}}
+    for key, name in KERNEL_NAMES.items():
+        kf = [v for k, v in fetch.items() if name in k]
+        kw = [v for k, v in write.items() if name in k]
+        if kf and kw:
+            ent[key] = {"fetch_bytes": kf[0] * 1024.0 * f_fetch, "write_bytes": kw[0] * 1024.0 * f_write,
+                        "fetch_kib_raw": kf[0], "write_kib_raw": kw[0]}
+    try:
+        with open(TRAFFIC_JSON) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        d = {}
+    d[workload] = ent
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: ent}))
 
 
 def run_workload(cfg, hw, dw, steps, warmup):
@@ -150,8 +198,8 @@ def summarize(cfg, r, steps, warmup):
         "layer": {"tflops": layer_flops / (ms / 1e3) / 1e12, "mfma_frac": layer_flops / (ms / 1e3) / 1e12 /
                   PEAK_BF16_TFLOPS, "alg_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms / 1e3) / 1e9,
                   "hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
-        "gate_up": roofline(gu_f, gu_b, gu_ms / 1e3, load_traffic(cfg.name)),
-        "down": roofline(dn_f, dn_b, dn_ms / 1e3),
+        "gate_up": roofline(gu_f, gu_b, gu_ms / 1e3, load_traffic(cfg.name, "gate_up")),
+        "down": roofline(dn_f, dn_b, dn_ms / 1e3, load_traffic(cfg.name, "down")),
         "experts_touched": r["n_touched"],
         "max_expert_load": int(r["counts"].max()),
         "empty_experts": int((r["counts"] == 0).sum()),
@@ -201,7 +249,14 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB")
+    ap.add_argument("--ingest-pmc", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV",
+                                                      "CALIB_MIB"),
+                    help="record counter runs of --workload into profiles/traffic.json (no GPU needed)")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        a = args.ingest_pmc
+        ingest_counters(args.workload, a[0], a[1], a[2], a[3], int(a[4]))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
