@@ -31,7 +31,12 @@ bool shape_valid(const beam_moe_shape* s) {
 // 128-wide unrolled groups and cover N in 128 (gate/up) or 256 (down) column blocks.
 bool route_supported(const beam_moe_shape* s) { return s->dtype != BEAM_BF16 || s->H % 128 == 0; }
 bool shape_supported(const beam_moe_shape* s) {
-    if (s->dtype == BEAM_BF16) return s->H % 256 == 0 && s->I % 128 == 0;
+    if (s->dtype == BEAM_BF16) {
+        // the GEMMs address token rows and h rows with 32-bit byte offsets
+        const int64_t P = s->T * s->top_k;
+        return s->H % 256 == 0 && s->I % 128 == 0 && s->T * (int64_t)s->H * 2 < ((int64_t)1 << 32) &&
+               P * (int64_t)s->I * 2 < ((int64_t)1 << 32);
+    }
     return true;
 }
 
@@ -217,7 +222,7 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
     void* h = at<void>(ws, L.h);
     void* ypair = at<void>(ws, L.ypair);
     if (bf16) {
-        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, H, I, K, sorted, tiles, ntiles, L.max_tiles,
+        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, T, H, I, E, K, sorted, tiles, ntiles, L.max_tiles,
                                       L.tile_rows, h, s));
     } else {
         BEAM_TRY(beam::launch_gate_up_f32(static_cast<const float*>(act), static_cast<const float*>(w_gate),
@@ -226,7 +231,8 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
     }
     BEAM_TRY(mark(BEAM_STAGE_DOWN));
     if (bf16) {
-        BEAM_TRY(beam::launch_down(h, true, w_down, H, I, sorted, tiles, ntiles, L.max_tiles, L.tile_rows, ypair, s));
+        BEAM_TRY(beam::launch_down(h, true, w_down, P, H, I, E, sorted, tiles, ntiles, L.max_tiles, L.tile_rows,
+                                   ypair, s));
     } else {
         BEAM_TRY(beam::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w_down), H, I, sorted,
                                        idx, P, static_cast<float*>(ypair), s));

@@ -379,38 +379,324 @@ __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t*
         run_tile<GATED, 1, 4>(c, lds);
 }
 
+// ---------------------------------------------------------------------------------
+// Line-streaming variant for prefill-sized tiles.  Work item and tile are as above (up
+// to 288 rows; 128 h columns for gate/up, 256 output columns for down); a work-group
+// of WAVES waves gives each wave NB 16-row weight blocks (gate/up: NB/2 gate blocks and
+// the up blocks of the same h columns).
+//
+// K advances 64 per step.  Weights: for each block a lane loads the 16-byte chunks
+// 2*(lane>>4) and 2*(lane>>4)+1 of its row's 128-byte window, so every block reads
+// whole cache lines each step; the even MFMA of a step takes the first chunk, the odd
+// MFMA the second, and the activation fragments use the same k order.  Weight loads
+// run RING-1 steps ahead in a ring of RING register sets.  Activations: the rows of
+// step kt+1 are written into one of two LDS buffers while step kt is multiplied out of
+// the other, and one barrier per step publishes them.  The LDS writes and every global
+// load of a step are spread over its MFMA sequence.  Buffer loads with 32-bit offsets
+// keep one address register per weight stream.
+// ---------------------------------------------------------------------------------
+constexpr int WKS = 64;                    // k per step
+constexpr int WBUF_ELEMS = GROWS * WKS;    // one LDS activation buffer (36 KB)
+constexpr int BUF_DWORD3 = 0x00020000;     // raw buffer descriptor word 3 on gfx9
+
+// LDS element offset of 16-byte chunk `ch` (0..7) of activation row `row` (128-byte
+// rows).  Any 16 consecutive rows at a fixed chunk, and any two rows' 8 chunks, fall in
+// 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int w_off(int row, int ch) { return row * WKS + ((ch ^ ((row >> 1) & 7)) << 3); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, BUF_DWORD3);
+}
+
+__device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+struct LineCtx {
+    __amdgpu_buffer_rsrc_t act;   // activation tensor (token rows or h rows)
+    __amdgpu_buffer_rsrc_t w0;    // weight blocks [0, NB/2)
+    __amdgpu_buffer_rsrc_t w1;    // weight blocks [NB/2, NB)
+    uint32_t wvoff;               // this lane's byte offset inside a weight block
+    int K, top_k, row_begin, row_count;
+    bool gather;
+    const int32_t* sorted_pairs;
+};
+
+template <int WAVES, int NB, int RING, int NRB>
+__device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][NB]) {
+    constexpr int THREADS = WAVES * 64;
+    constexpr int ACH = NRB * 16 * 8;                  // 16-byte activation chunks per step
+    constexpr int AL = (ACH + THREADS - 1) / THREADS;
+    constexpr int NOPS = 2 * AL + NB;                  // memory operations spread over a step
+    constexpr int HB = NB / 2;                         // blocks per weight descriptor
+    constexpr int UNR = RING % 2 ? 2 * RING : RING;    // ring slot and LDS buffer both static
+    const int lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int nk = c.K / WKS;
+    const uint32_t wblk = (uint32_t)(16 * c.K * 2);
+
+    // activation staging: chunk q = tid + THREADS*i (wrapped for partial tiles)
+    uint32_t avoff[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int q = (tid + i * THREADS) % ACH;
+        const int row = q >> 3, ch = q & 7;
+        const int src = row < c.row_count ? row : 0;
+        const int64_t r = c.gather ? (int64_t)(c.sorted_pairs[c.row_begin + src] / c.top_k)
+                                   : (int64_t)(c.row_begin + src);
+        avoff[i] = (uint32_t)((r * c.K + ch * 8) * 2);
+    }
+    auto lds_slot = [&](int i) {
+        const int q = (tid + i * THREADS) % ACH;
+        return w_off(q >> 3, q & 7);
+    };
+    u32x4 sa[AL];
+    u32x4 rb[RING][NB][2];
+    auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
+    auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
+    auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
+    auto load_b = [&](int b, int kstep, int set) {
+        const __amdgpu_buffer_rsrc_t r = b < HB ? c.w0 : c.w1;
+        const uint32_t so = kbytes(kstep) + (uint32_t)(b % HB) * wblk;
+        rb[set][b][0] = buf_load(r, c.wvoff, so);
+        rb[set][b][1] = buf_load(r, c.wvoff + 16, so);
+    };
+    // fragment read offsets: row r*16 + (lane & 15), chunks 2g and 2g+1 (g = lane >> 4)
+    const int fr = lane & 15, g = lane >> 4;
+    const int off_e = fr * WKS + (((2 * g) ^ ((fr >> 1) & 7)) << 3);
+    const int off_o = fr * WKS + (((2 * g + 1) ^ ((fr >> 1) & 7)) << 3);
+#ifndef LINE_LA
+#define LINE_LA 1
+#endif
+    constexpr int LA = NRB < LINE_LA ? NRB : LINE_LA;  // fragment lookahead (row blocks)
+
+    // memory operation o of a step: o < 2*AL alternates (write chunk o/2 of step kt+1,
+    // load chunk o/2 of step kt+2); then the weight loads of step kt+RING-1, a block each
+    auto mem_op = [&](int o, int kt, int wbuf, int set) {
+        if (o < 2 * AL) {
+            if ((o & 1) == 0)
+                store_a(o >> 1, wbuf);
+            else
+                load_a(o >> 1, kt + 2);
+        } else {
+            load_b(o - 2 * AL, kt + RING - 1, set);
+        }
+    };
+
+    auto step = [&](int kt, auto jc) {
+        constexpr int j = decltype(jc)::value;          // kt mod UNR
+        constexpr int set = j % RING;
+        constexpr int nset = (j + RING - 1) % RING;     // ring slot of step kt+RING-1
+        const uint16_t* L = lds + (j & 1) * WBUF_ELEMS;
+        const int wbuf = (j + 1) & 1;
+        lds_barrier();
+        bf16x8 ae[NRB], ao[NRB];
+#pragma unroll
+        for (int r = 0; r < LA; ++r) {
+            ae[r] = *(const bf16x8*)(L + off_e + r * 16 * WKS);
+            ao[r] = *(const bf16x8*)(L + off_o + r * 16 * WKS);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            if (r + LA < NRB) {
+                ae[r + LA] = *(const bf16x8*)(L + off_e + (r + LA) * 16 * WKS);
+                ao[r + LA] = *(const bf16x8*)(L + off_o + (r + LA) * 16 * WKS);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const bf16x8 bw = __builtin_bit_cast(bf16x8, rb[set][b][0]);
+                acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae[r], bw, acc[r][b], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+            // this row block's share of the step's memory operations
+#pragma unroll
+            for (int o = 0; o < NOPS; ++o) {
+                if (o >= (r * NOPS) / NRB && o < ((r + 1) * NOPS) / NRB) {
+                    mem_op(o, kt, wbuf, nset);
+                    if (o < 2 * AL && (o & 1) == 0)
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    else if (o < 2 * AL)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    else
+                        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const bf16x8 bw = __builtin_bit_cast(bf16x8, rb[set][b][1]);
+                acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao[r], bw, acc[r][b], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+        }
+    };
+
+    // prologue: step 0 in buffer 0, step 1 staged in registers, weights of the first
+    // RING-1 steps in flight
+#pragma unroll
+    for (int i = 0; i < AL; ++i) load_a(i, 0);
+#pragma unroll
+    for (int i = 0; i < AL; ++i) store_a(i, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < AL; ++i) load_a(i, 1);
+#pragma unroll
+    for (int s2 = 0; s2 < RING - 1; ++s2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) load_b(b, s2, s2);
+    __builtin_amdgcn_sched_barrier(0);
+    int kt = 0;
+    for (; kt + UNR <= nk; kt += UNR) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            (step(kt + J, std::integral_constant<int, J>()), ...);
+        }(std::make_integer_sequence<int, UNR>());
+    }
+    // remainder: nk is even and nk - kt < UNR <= 6
+    if (nk - kt >= 2) {
+        step(kt, std::integral_constant<int, 0>());
+        step(kt + 1, std::integral_constant<int, 1>());
+    }
+    if (UNR > 4 && nk - kt >= 4) {
+        step(kt + 2, std::integral_constant<int, 2 % UNR>());
+        step(kt + 3, std::integral_constant<int, 3 % UNR>());
+    }
+}
+
+template <bool GATED, int WAVES, int NB, int RING>
+__global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
+    const uint16_t* __restrict__ A, uint32_t a_bytes, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, int K, int N, int top_k, const int32_t* __restrict__ sorted_pairs,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_col_blocks,
+    uint16_t* __restrict__ C) {
+    static_assert(WAVES * NB * 16 == 256 && NB % 2 == 0, "a work-group covers 256 weight rows");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * WBUF_ELEMS];
+
+    const int work = *num_tiles * n_col_blocks;
+    const int per_xcd = (work + 7) >> 3;
+    const int slot = (int)(blockIdx.x >> 3);
+    if (slot >= per_xcd) return;
+    const int item = (int)(blockIdx.x & 7) * per_xcd + slot;
+    if (item >= work) return;
+    const TileEntry te = tiles[item / n_col_blocks];
+    const int cblk = item % n_col_blocks;
+    if (te.row_count <= 0) return;
+    const int64_t e = te.expert;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int HB = NB / 2;
+
+    LineCtx c;
+    c.act = make_rsrc(A, a_bytes);
+    c.K = K;
+    c.top_k = top_k;
+    c.row_begin = te.row_begin;
+    c.row_count = te.row_count;
+    c.gather = GATED;
+    c.sorted_pairs = sorted_pairs;
+    c.wvoff = (uint32_t)(((lane & 15) * K + (lane >> 4) * 16) * 2);
+    const uint32_t bytes = (uint32_t)(HB * 16 * K * 2);
+    int col0;
+    if (GATED) {
+        col0 = cblk * (WAVES * HB * 16) + wave * (HB * 16);  // h columns [col0, col0 + 16*HB)
+        c.w0 = make_rsrc(B0 + (e * N + col0) * (int64_t)K, bytes);
+        c.w1 = make_rsrc(B1 + (e * N + col0) * (int64_t)K, bytes);
+    } else {
+        col0 = cblk * (WAVES * NB * 16) + wave * (NB * 16);  // output columns [col0, col0 + 16*NB)
+        c.w0 = make_rsrc(B0 + (e * N + col0) * (int64_t)K, bytes);
+        c.w1 = make_rsrc(B0 + (e * N + col0 + HB * 16) * (int64_t)K, bytes);
+    }
+
+    auto run = [&](auto nrbc) {
+        constexpr int NRB = decltype(nrbc)::value;
+        f32x4 acc[NRB][NB];
+#pragma unroll
+        for (int r = 0; r < NRB; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        line_body<WAVES, NB, RING, NRB>(c, lds, acc);
+        // epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15)
+#pragma unroll
+        for (int r = 0; r < NRB; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = r * 16 + 4 * (lane >> 4) + q;
+                if (m >= c.row_count) continue;
+                if (GATED) {
+                    uint16_t* hrow = C + (int64_t)(c.row_begin + m) * N + col0 + (lane & 15);
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) {
+                        const float gv = acc[r][hb][q], uv = acc[r][HB + hb][q];
+                        hrow[16 * hb] = f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv);
+                    }
+                } else {
+                    const int64_t p = c.sorted_pairs[c.row_begin + m];
+                    uint16_t* yrow = C + p * N + col0 + (lane & 15);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) yrow[16 * b] = f32_to_bf16(acc[r][b][q]);
+                }
+            }
+    };
+    const int nrb = (te.row_count + 15) >> 4;
+    if (nrb > 16)
+        run(std::integral_constant<int, 18>());
+    else if (nrb > 12)
+        run(std::integral_constant<int, 16>());
+    else if (nrb > 8)
+        run(std::integral_constant<int, 12>());
+    else if (nrb > 4)
+        run(std::integral_constant<int, 8>());
+    else if (nrb > 2)
+        run(std::integral_constant<int, 4>());
+    else
+        run(std::integral_constant<int, 2>());
+}
+
+#ifndef LINE_WAVES
+#define LINE_WAVES 8
+#define LINE_NB 2
+#define LINE_RING 3
+#endif
+
 int gemm_tile_rows(int64_t P, int E, bool bf16) {
     (void)P;
     (void)E;
     return bf16 ? GROWS : (1 << 30);  // the fp32 path does not use tiles
 }
 
+// Average rows per expert from which the wide kernel is used (below it the weight
+// stream dominates and the 8-wave kernel's decode variant is faster).
+constexpr int64_t WIDE_MIN_ROWS_PER_EXPERT = 64;
+
 template <bool GATED>
-static void launch_gemm(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int K, int N, int top_k,
-                        const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
-                        int64_t max_tile_count, uint16_t* C, hipStream_t s) {
-    const int ncols = GATED ? GWAVES * 16 : GWAVES * 32;
+static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint16_t* B0, const uint16_t* B1, int K, int N,
+                        int top_k, int64_t P, int E, const int32_t* sorted_pairs, const TileEntry* tiles,
+                        const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C, hipStream_t s) {
+    const int ncols = GATED ? GWAVES * 16 : GWAVES * 32;  // same column blocks in both kernels
     const int ncb = N / ncols;
     const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-    moe_gemm_bf16_kernel<GATED><<<(unsigned)blocks, GTHREADS, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs, tiles,
-                                                                     num_tiles, ncb, C);
+    if (P >= WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0)
+        moe_gemm_line_kernel<GATED, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
+            A, (uint32_t)a_bytes, B0, B1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
+    else
+        moe_gemm_bf16_kernel<GATED><<<(unsigned)blocks, GTHREADS, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs,
+                                                                         tiles, num_tiles, ncb, C);
 }
 
-hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int H, int I, int top_k,
-                          const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
-                          int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
+hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int64_t T, int H, int I,
+                          int E, int top_k, const int32_t* sorted_pairs, const TileEntry* tiles,
+                          const int32_t* num_tiles, int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
-    launch_gemm<true>((const uint16_t*)act, (const uint16_t*)w_gate, (const uint16_t*)w_up, H, I, top_k, sorted_pairs,
-                      tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
+    launch_gemm<true>((const uint16_t*)act, (uint64_t)T * H * 2, (const uint16_t*)w_gate, (const uint16_t*)w_up, H, I,
+                      top_k, T * top_k, E, sorted_pairs, tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, int H, int I, const int32_t* sorted_pairs,
-                       const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, int tile_rows,
-                       void* y_pair, hipStream_t s) {
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, int64_t P, int H, int I, int E,
+                       const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+                       int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
-    launch_gemm<false>((const uint16_t*)h, (const uint16_t*)w_down, nullptr, I, H, 0, sorted_pairs, tiles, num_tiles,
-                       max_tile_count, (uint16_t*)y_pair, s);
+    launch_gemm<false>((const uint16_t*)h, (uint64_t)P * I * 2, (const uint16_t*)w_down, nullptr, I, H, 0, P, E,
+                       sorted_pairs, tiles, num_tiles, max_tile_count, (uint16_t*)y_pair, s);
     return hipGetLastError();
 }
 
