@@ -400,9 +400,12 @@ constexpr int WBUF_ELEMS = GROWS * WKS;    // one LDS activation buffer (36 KB)
 constexpr int BUF_DWORD3 = 0x00020000;     // raw buffer descriptor word 3 on gfx9
 
 // LDS element offset of 16-byte chunk `ch` (0..7) of activation row `row` (128-byte
-// rows).  Any 16 consecutive rows at a fixed chunk, and any two rows' 8 chunks, fall in
-// 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int w_off(int row, int ch) { return row * WKS + ((ch ^ ((row >> 1) & 7)) << 3); }
+// rows).  The XOR pattern makes the fragment reads (16 consecutive rows at one chunk per
+// 16 lanes) free of bank conflicts on gfx950; it was chosen among candidate patterns with
+// the LDS bank-conflict counter (patterns such as row & 7 or (row >> 1) & 7 conflict
+// 2-way).  Writes cover whole 128-byte rows, which any in-row permutation keeps intact.
+__device__ __forceinline__ int w_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int w_off(int row, int ch) { return row * WKS + ((ch ^ w_swz(row)) << 3); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, BUF_DWORD3);
@@ -422,17 +425,39 @@ struct LineCtx {
     const int32_t* sorted_pairs;
 };
 
+// Weight loads of step `kstep` of a work item into ring slot `set` (steps past the end
+// reload the last step, which the cache still holds).
+template <int NB, int RING>
+__device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], int b, int kstep, int set) {
+    constexpr int HB = NB / 2;
+    const int nk = c.K / WKS;
+    const uint32_t so = (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2) + (uint32_t)(b % HB) * (uint32_t)(16 * c.K * 2);
+    const __amdgpu_buffer_rsrc_t r = b < HB ? c.w0 : c.w1;
+    rb[set][b][0] = buf_load(r, c.wvoff, so);
+    rb[set][b][1] = buf_load(r, c.wvoff + 16, so);
+}
+
+// The weights of a work item's first RING-1 steps (issued before the previous item's
+// epilogue, so the stream does not stop between items).
+template <int NB, int RING>
+__device__ __forceinline__ void line_prologue_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2]) {
+#pragma unroll
+    for (int s2 = 0; s2 < RING - 1; ++s2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) line_load_b<NB, RING>(c, rb, b, s2, s2);
+}
+
+// Main loop of one work item; the caller has issued its first RING-1 weight steps.
 template <int WAVES, int NB, int RING, int NRB>
-__device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][NB]) {
+__device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4 (&rb)[RING][NB][2],
+                                          f32x4 (&acc)[NRB][NB]) {
     constexpr int THREADS = WAVES * 64;
     constexpr int ACH = NRB * 16 * 8;                  // 16-byte activation chunks per step
     constexpr int AL = (ACH + THREADS - 1) / THREADS;
     constexpr int NOPS = 2 * AL + NB;                  // memory operations spread over a step
-    constexpr int HB = NB / 2;                         // blocks per weight descriptor
     constexpr int UNR = RING % 2 ? 2 * RING : RING;    // ring slot and LDS buffer both static
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int nk = c.K / WKS;
-    const uint32_t wblk = (uint32_t)(16 * c.K * 2);
 
     // activation staging: chunk q = tid + THREADS*i (wrapped for partial tiles)
     uint32_t avoff[AL];
@@ -450,20 +475,14 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, f32x4
         return w_off(q >> 3, q & 7);
     };
     u32x4 sa[AL];
-    u32x4 rb[RING][NB][2];
     auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
     auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
     auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
-    auto load_b = [&](int b, int kstep, int set) {
-        const __amdgpu_buffer_rsrc_t r = b < HB ? c.w0 : c.w1;
-        const uint32_t so = kbytes(kstep) + (uint32_t)(b % HB) * wblk;
-        rb[set][b][0] = buf_load(r, c.wvoff, so);
-        rb[set][b][1] = buf_load(r, c.wvoff + 16, so);
-    };
+    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING>(c, rb, b, kstep, set); };
     // fragment read offsets: row r*16 + (lane & 15), chunks 2g and 2g+1 (g = lane >> 4)
     const int fr = lane & 15, g = lane >> 4;
-    const int off_e = fr * WKS + (((2 * g) ^ ((fr >> 1) & 7)) << 3);
-    const int off_o = fr * WKS + (((2 * g + 1) ^ ((fr >> 1) & 7)) << 3);
+    const int off_e = w_off(fr, 2 * g);
+    const int off_o = w_off(fr, 2 * g + 1);
 #ifndef LINE_LA
 #define LINE_LA 1
 #endif
@@ -531,8 +550,8 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, f32x4
         }
     };
 
-    // prologue: step 0 in buffer 0, step 1 staged in registers, weights of the first
-    // RING-1 steps in flight
+    // prologue: step 0 in buffer 0, step 1 staged in registers (the weights of the first
+    // RING-1 steps are already in flight)
 #pragma unroll
     for (int i = 0; i < AL; ++i) load_a(i, 0);
 #pragma unroll
@@ -540,10 +559,6 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, f32x4
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < AL; ++i) load_a(i, 1);
-#pragma unroll
-    for (int s2 = 0; s2 < RING - 1; ++s2)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) load_b(b, s2, s2);
     __builtin_amdgcn_sched_barrier(0);
     int kt = 0;
     for (; kt + UNR <= nk; kt += UNR) {
@@ -569,8 +584,16 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     const TileEntry* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_col_blocks,
     uint16_t* __restrict__ C) {
     static_assert(WAVES * NB * 16 == 256 && NB % 2 == 0, "a work-group covers 256 weight rows");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * WBUF_ELEMS];
+    // the output tile is staged through LDS (rows padded by 16 bytes) once the main loop is done
+    constexpr int EPI_COLS = GATED ? WAVES * (NB / 2) * 16 : WAVES * NB * 16;
+    constexpr int EPI_STRIDE = EPI_COLS + 8;
+    constexpr int LDS_ELEMS = GROWS * EPI_STRIDE > 2 * WBUF_ELEMS ? GROWS * EPI_STRIDE : 2 * WBUF_ELEMS;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+    constexpr int HB = NB / 2;
 
+    // XCD-aware order (blocks are dealt to the 8 XCDs round-robin): each XCD takes a
+    // contiguous run of work items, so the column blocks of one tile share its activation
+    // rows in that XCD's L2.
     const int work = *num_tiles * n_col_blocks;
     const int per_xcd = (work + 7) >> 3;
     const int slot = (int)(blockIdx.x >> 3);
@@ -583,7 +606,6 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     const int64_t e = te.expert;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    constexpr int HB = NB / 2;
 
     LineCtx c;
     c.act = make_rsrc(A, a_bytes);
@@ -608,33 +630,48 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
 
     auto run = [&](auto nrbc) {
         constexpr int NRB = decltype(nrbc)::value;
+        u32x4 rb[RING][NB][2];
+        line_prologue_b<NB, RING>(c, rb);
         f32x4 acc[NRB][NB];
 #pragma unroll
         for (int r = 0; r < NRB; ++r)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        line_body<WAVES, NB, RING, NRB>(c, lds, acc);
-        // epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15)
+        line_body<WAVES, NB, RING, NRB>(c, lds, rb, acc);
+        // epilogue: each wave writes its bf16 columns of the tile into LDS (C layout of a
+        // 16x16 block: rows 4*(lane>>4)+q, column lane&15), then the work-group stores
+        // whole 16-byte chunks of every output row.  silu(g) = g / (1 + e^-g) with the
+        // hardware reciprocal (the result is rounded to bf16).
+        lds_barrier();  // every wave is done with the activation buffers
+        const int wcol = col0 - cblk * EPI_COLS;
 #pragma unroll
         for (int r = 0; r < NRB; ++r)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int m = r * 16 + 4 * (lane >> 4) + q;
-                if (m >= c.row_count) continue;
+                uint16_t* lrow = lds + (r * 16 + 4 * (lane >> 4) + q) * EPI_STRIDE + wcol + (lane & 15);
                 if (GATED) {
-                    uint16_t* hrow = C + (int64_t)(c.row_begin + m) * N + col0 + (lane & 15);
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb) {
                         const float gv = acc[r][hb][q], uv = acc[r][HB + hb][q];
-                        hrow[16 * hb] = f32_to_bf16(gv / (1.0f + __expf(-gv)) * uv);
+                        lrow[16 * hb] = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
                     }
                 } else {
-                    const int64_t p = c.sorted_pairs[c.row_begin + m];
-                    uint16_t* yrow = C + p * N + col0 + (lane & 15);
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) yrow[16 * b] = f32_to_bf16(acc[r][b][q]);
+                    for (int b = 0; b < NB; ++b) lrow[16 * b] = f32_to_bf16(acc[r][b][q]);
                 }
             }
+        lds_barrier();
+        constexpr int CPR = EPI_COLS / 8;  // 16-byte chunks per output row
+#pragma unroll
+        for (int q0 = 0; q0 < NRB * 16 * CPR; q0 += WAVES * 64) {
+            const int q = q0 + (int)threadIdx.x;
+            const int row = q / CPR, ch = q % CPR;
+            if (q < NRB * 16 * CPR && row < c.row_count) {
+                const u32x4 v = *(const u32x4*)(lds + row * EPI_STRIDE + ch * 8);
+                const int64_t orow = GATED ? (int64_t)(c.row_begin + row) : (int64_t)c.sorted_pairs[c.row_begin + row];
+                *(u32x4*)(C + orow * N + cblk * EPI_COLS + ch * 8) = v;
+            }
+        }
     };
     const int nrb = (te.row_count + 15) >> 4;
     if (nrb > 16)
