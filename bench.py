@@ -84,7 +84,8 @@ def load_traffic(workload, kernel):
         return None
 
 
-KERNEL_NAMES = {"gate_up": "moe_gemm_bf16_kernel<true>", "down": "moe_gemm_bf16_kernel<false>"}
+# expert GEMM kernels (the 8-wave decode kernel or the line-streaming prefill kernel) by template flag
+KERNEL_NAMES = {"gate_up": "<true", "down": "<false"}
 
 
 def _counter_means(path, counter):
@@ -113,8 +114,8 @@ def ingest_counters(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write
     ent = {"experts_hip_sha256_16": kernel_source_hash(),
            "calibration": {"copy_bytes": n, "fetch_factor": f_fetch, "write_factor": f_write}}
     for key, name in KERNEL_NAMES.items():
-        kf = [v for k, v in fetch.items() if name in k]
-        kw = [v for k, v in write.items() if name in k]
+        kf = [v for k, v in fetch.items() if "moe_gemm" in k and name in k]
+        kw = [v for k, v in write.items() if "moe_gemm" in k and name in k]
         if kf and kw:
             ent[key] = {"fetch_bytes": kf[0] * 1024.0 * f_fetch, "write_bytes": kw[0] * 1024.0 * f_write,
                         "fetch_kib_raw": kf[0], "write_kib_raw": kw[0]}
