@@ -415,6 +415,7 @@ __device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t vof
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+
 struct LineCtx {
     __amdgpu_buffer_rsrc_t act;   // activation tensor (token rows or h rows)
     __amdgpu_buffer_rsrc_t w0;    // weight blocks [0, NB/2)

@@ -23,13 +23,15 @@ namespace beam {
 // and the selection kernel adds the partials in split order before rounding the logit
 // once to fp32, so the result does not depend on scheduling.
 //
-// Work-group: 4 waves, 32 tokens x 128 experts; wave w owns experts [32w, 32w+32).
-// Operands are read straight from global memory (the matrix is cache-resident), with
-// the loads of the next RL_RING-1 steps in flight.
+// Work-group: 4 waves, 64 tokens x 128 experts; wave w owns experts [32w, 32w+32) of
+// all 64 tokens, so each split of a router weight feeds 4 row blocks.  Operands are
+// read straight from global memory (the matrix is cache-resident), with the loads of
+// the next step in flight.
 // ---------------------------------------------------------------------------------
-constexpr int RL_TOK = 32;
-constexpr int RL_EXP = 128;
-constexpr int RL_RING = 4;
+constexpr int RL_TOK = 64;           // tokens per work-group
+constexpr int RL_RB = RL_TOK / 16;   // 16-row MFMA blocks per wave
+constexpr int RL_EXP = 128;          // experts per work-group (32 per wave)
+constexpr int RL_RING = 2;           // register sets: the next step's loads are in flight
 
 __device__ __forceinline__ void split3(float w, float& hi, float& mid, float& lo) {
     hi = __uint_as_float(__float_as_uint(w) & 0xFFFF0000u);
@@ -45,7 +47,7 @@ __device__ __forceinline__ __bf16 as_bf16_trunc(float f) {
 
 // x [T,H] bf16, wr [E,H] fp32 -> part [nsplit][T][E] fp64 (split s covers columns
 // [s*klen, (s+1)*klen), klen a multiple of 32 * RL_RING).
-__global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t* __restrict__ x,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) router_logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr, int64_t T, int H,
                                                                  int E, int klen, double* __restrict__ part) {
     const int lane = threadIdx.x & 63;
@@ -56,9 +58,9 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
     if (e0 >= E) return;  // whole wave idle (uniform)
 
     const int kq = (lane >> 4) * 8 + split * klen;  // k offset of this lane
-    const uint16_t* arow[2];
+    const uint16_t* arow[RL_RB];
     const float* brow[2];
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RL_RB; ++rb) {
         const int64_t t = t0 + rb * 16 + (lane & 15);
         arow[rb] = x + (t < T ? t : T - 1) * (int64_t)H + kq;  // rows past T repeat row T-1
     }
@@ -67,18 +69,18 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
         brow[cb] = wr + (int64_t)(e < E ? e : E - 1) * H + kq;
     }
 
-    f32x4 acc[2][2];
-    double acc64[2][2][4];
-    for (int i = 0; i < 2; ++i)
+    f32x4 acc[RL_RB][2];
+    double acc64[RL_RB][2][4];
+    for (int i = 0; i < RL_RB; ++i)
         for (int j = 0; j < 2; ++j)
             for (int q = 0; q < 4; ++q) acc64[i][j][q] = 0.0;
 
-    u32x4 ra[RL_RING][2];
+    u32x4 ra[RL_RING][RL_RB];
     f32x4 rw[RL_RING][2][2];
     const int nks = klen / 32;
     auto load = [&](int ks, int set) {
         const int k0 = (ks < nks ? ks : nks - 1) * 32;
-        for (int rb = 0; rb < 2; ++rb) ra[set][rb] = *(const u32x4*)(arow[rb] + k0);
+        for (int rb = 0; rb < RL_RB; ++rb) ra[set][rb] = *(const u32x4*)(arow[rb] + k0);
         for (int cb = 0; cb < 2; ++cb) {
             rw[set][cb][0] = *(const f32x4*)(brow[cb] + k0);
             rw[set][cb][1] = *(const f32x4*)(brow[cb] + k0 + 4);
@@ -86,10 +88,10 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
     };
     auto step = [&](int ks, int set) {
         load(ks + RL_RING - 1, (set + RL_RING - 1) % RL_RING);
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < RL_RB; ++i)
             for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 a[2];
-        for (int rb = 0; rb < 2; ++rb) a[rb] = __builtin_bit_cast(bf16x8, ra[set][rb]);
+        bf16x8 a[RL_RB];
+        for (int rb = 0; rb < RL_RB; ++rb) a[rb] = __builtin_bit_cast(bf16x8, ra[set][rb]);
         for (int cb = 0; cb < 2; ++cb) {
             bf16x8 bh, bm, bl;
             for (int q = 0; q < 8; ++q) {
@@ -100,7 +102,7 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
                 bm[q] = as_bf16_trunc(mid);
                 bl[q] = as_bf16_trunc(lo);
             }
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RL_RB; ++rb) {
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bl, acc[rb][cb], 0, 0, 0);
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bm, acc[rb][cb], 0, 0, 0);
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bh, acc[rb][cb], 0, 0, 0);
@@ -108,20 +110,19 @@ __global__ void __launch_bounds__(256) router_logits_bf16_kernel(const uint16_t*
         }
         // fold each 32-term block into fp64: the matrix-core sum rounds once per
         // instruction, so short fp32 chains keep the logit error near one fp32 ulp
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < RL_RB; ++i)
             for (int j = 0; j < 2; ++j)
                 for (int q = 0; q < 4; ++q) acc64[i][j][q] += (double)acc[i][j][q];
     };
     for (int s = 0; s < RL_RING - 1; ++s) load(s, s);
-    for (int ks = 0; ks < nks; ks += RL_RING) {  // nks is a multiple of RL_RING
-        step(ks, 0);
-        step(ks + 1, 1);
-        step(ks + 2, 2);
-        step(ks + 3, 3);
+    static_assert(4 % RL_RING == 0, "nks is a multiple of 4");
+    for (int ks = 0; ks < nks; ks += RL_RING) {
+#pragma unroll
+        for (int j = 0; j < RL_RING; ++j) step(ks + j, j);
     }
     // C layout of a 16x16 MFMA block: lane holds rows 4*(lane>>4)+q, column lane&15
     double* out = part + (int64_t)split * T * E;
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RL_RB; ++rb)
         for (int cb = 0; cb < 2; ++cb) {
             const int e = e0 + cb * 16 + (lane & 15);
             for (int q = 0; q < 4; ++q) {
