@@ -484,10 +484,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     const int fr = lane & 15, g = lane >> 4;
     const int off_e = w_off(fr, 2 * g);
     const int off_o = w_off(fr, 2 * g + 1);
-#ifndef LINE_LA
-#define LINE_LA 1
-#endif
-    constexpr int LA = NRB < LINE_LA ? NRB : LINE_LA;  // fragment lookahead (row blocks)
+    constexpr int LA = 1;  // fragment lookahead (row blocks); deeper measured no faster
 
     // memory operation o of a step: o < 2*AL alternates (write chunk o/2 of step kt+1,
     // load chunk o/2 of step kt+2); then the weight loads of step kt+RING-1, a block each
@@ -689,11 +686,11 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
         run(std::integral_constant<int, 2>());
 }
 
-#ifndef LINE_WAVES
-#define LINE_WAVES 8
-#define LINE_NB 2
-#define LINE_RING 3
-#endif
+// prefill configuration: 8 waves x 2 weight blocks (256 weight rows per work-group),
+// weights one step ahead (a deeper ring measured no faster and costs 16 registers)
+constexpr int LINE_WAVES = 8;
+constexpr int LINE_NB = 2;
+constexpr int LINE_RING = 2;
 
 int gemm_tile_rows(int64_t P, int E, bool bf16) {
     (void)P;

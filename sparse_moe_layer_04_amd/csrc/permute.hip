@@ -10,7 +10,7 @@
 
 namespace beam {
 
-constexpr int PERM_CHUNK = 4096;
+constexpr int PERM_CHUNK = 1024;
 constexpr int PERM_MAX_E = 1024;
 
 size_t permute_scratch_words(int64_t P, int E) {
@@ -34,55 +34,78 @@ __global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One work-group of 1024 threads.
+// One work-group of 1024 threads.  Thread t handles expert t % E for chunk group
+// t / E (G = 1024 / E groups of consecutive chunks), so the per-expert scan over
+// chunks runs in G pieces with coalesced reads of the count rows.
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ counts, int nchunks, int E, int64_t P,
                                                          int32_t* __restrict__ offsets, TileEntry* __restrict__ tiles,
                                                          int32_t* __restrict__ num_tiles, int tile_rows) {
+    __shared__ int32_t part[1024];  // [group][expert] chunk-range sums, then group bases
     __shared__ int32_t tot[PERM_MAX_E];
     __shared__ int32_t off[PERM_MAX_E];
     __shared__ int32_t ntl[PERM_MAX_E];
     __shared__ int32_t toff[PERM_MAX_E];
     const int tid = threadIdx.x;
-    // per expert: exclusive scan over chunks (in place) and the expert total
-    for (int e = tid; e < E; e += blockDim.x) {
-        int32_t run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            int32_t v = counts[(int64_t)c * E + e];
-            counts[(int64_t)c * E + e] = run;
-            run += v;
-        }
-        tot[e] = run;
-        ntl[e] = run > 0 ? (run + tile_rows - 1) / tile_rows : 0;
+    const int G = 1024 / E;  // >= 1 since E <= 1024
+    const int e = tid % E, g = tid / E;
+    const int cpg = (nchunks + G - 1) / G;
+    const int c0 = g * cpg, c1 = (g + 1) * cpg < nchunks ? (g + 1) * cpg : nchunks;
+    // (1) sum of each chunk range
+    if (g < G) {
+        int32_t sum = 0;
+        for (int c = c0; c < c1; ++c) sum += counts[(int64_t)c * E + e];
+        part[g * E + e] = sum;
     }
     __syncthreads();
-    // exclusive scans over experts (E <= 1024: a single pass by one thread is cheap)
+    // (2) per expert: exclusive scan over the groups and the expert total
+    if (tid < E) {
+        int32_t run = 0;
+        for (int gg = 0; gg < G; ++gg) {
+            const int32_t v = part[gg * E + tid];
+            part[gg * E + tid] = run;
+            run += v;
+        }
+        tot[tid] = run;
+        ntl[tid] = run > 0 ? (run + tile_rows - 1) / tile_rows : 0;
+    }
+    __syncthreads();
+    // (3) exclusive scans over experts (E <= 1024: a single pass by one thread is cheap)
     if (tid == 0) {
         int32_t a = 0, b = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = a;
-            a += tot[e];
-            toff[e] = b;
-            b += ntl[e];
+        for (int k = 0; k < E; ++k) {
+            off[k] = a;
+            a += tot[k];
+            toff[k] = b;
+            b += ntl[k];
         }
         offsets[E] = a;
         if (num_tiles) *num_tiles = b;
     }
     __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) {
-        offsets[e] = off[e];
-        for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += off[e];
+    // (4) every chunk's first row per expert: expert offset + earlier chunks' counts
+    if (g < G) {
+        int32_t run = off[e] + part[g * E + e];
+        for (int c = c0; c < c1; ++c) {
+            const int32_t v = counts[(int64_t)c * E + e];
+            counts[(int64_t)c * E + e] = run;
+            run += v;
+        }
+    }
+    // (5) expert offsets and the balanced tile list
+    for (int k = tid; k < E; k += blockDim.x) {
+        offsets[k] = off[k];
         if (tiles) {
-            int n = ntl[e];
+            const int n = ntl[k];
             if (n > 0) {
-                int c = tot[e];
-                int r = (c + n - 1) / n;  // balanced rows per tile, <= tile_rows
+                const int c = tot[k];
+                const int r = (c + n - 1) / n;  // balanced rows per tile, <= tile_rows
                 for (int j = 0; j < n; ++j) {
                     TileEntry te;
-                    te.expert = e;
-                    te.row_begin = off[e] + j * r;
+                    te.expert = k;
+                    te.row_begin = off[k] + j * r;
                     te.row_count = (c - j * r) < r ? (c - j * r) : r;
                     te.pad = 0;
-                    tiles[toff[e] + j] = te;
+                    tiles[toff[k] + j] = te;
                 }
             }
         }
