@@ -169,103 +169,125 @@ hipError_t launch_router_logits(const void* x, bool bf16, const float* w_router,
 }
 
 // ---------------------------------------------------------------------------------
-// Selection: one wave per token.  s = fp32(sigmoid(l)) evaluated in fp64 and rounded
-// once; s' = s + b (fp32); group score = sum of the group's two largest s' (fp32);
-// keep the topk_group best groups; top_k largest s' among their experts; every
-// comparison orders by value, then by lower index.  w = rho * s / sum(s) in fp32,
-// summed in choice order.
+// Selection.  s = fp32(sigmoid(l)) evaluated in fp64 and rounded once; s' = s + b
+// (fp32); group score = sum of the group's two largest s' (fp32); keep the topk_group
+// best groups; top_k largest s' among their experts; every comparison orders by value,
+// then by lower index.  w = rho * s / sum(s) in fp32, summed in choice order.
+// A work-group takes `tpb` tokens (4 for large T, else 1): all 256 threads reduce the
+// partial logits, then wave w chooses the experts of token w.
 // ---------------------------------------------------------------------------------
 constexpr int SEL_MAX_E = 1024;
 constexpr int SEL_MAX_G = 64;
-constexpr int SEL_WAVES = 4;
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_MAX_TPB = SEL_THREADS / 64;
 
 __device__ __forceinline__ bool ranks_before(float va, int a, float vb, int b) {
     return va > vb || (va == vb && a < b);
 }
 
-__global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const double* __restrict__ part, int nsplit,
-                                                                       const float* __restrict__ bias, int64_t T,
-                                                                       int E, int n_group, int topk_group,
-                                                                       int top_k, float rho,
-                                                                       int32_t* __restrict__ idx_out,
-                                                                       float* __restrict__ w_out,
-                                                                       float* __restrict__ logits_out) {
-    __shared__ float s_sc[SEL_WAVES][SEL_MAX_E];
-    __shared__ float s_sb[SEL_WAVES][SEL_MAX_E];
-    __shared__ float s_gs[SEL_WAVES][SEL_MAX_G];
-    __shared__ int s_kept[SEL_WAVES][SEL_MAX_G];
+__global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double* __restrict__ part, int nsplit,
+                                                                    const float* __restrict__ bias, int64_t T, int E,
+                                                                    int n_group, int topk_group, int top_k,
+                                                                    float rho, int tpb, int32_t* __restrict__ idx_out,
+                                                                    float* __restrict__ w_out,
+                                                                    float* __restrict__ logits_out) {
+    __shared__ float s_sc[SEL_MAX_TPB][SEL_MAX_E];
+    __shared__ float s_sb[SEL_MAX_TPB][SEL_MAX_E];
+    __shared__ float s_gs[SEL_MAX_TPB][SEL_MAX_G];
+    __shared__ int s_kept[SEL_MAX_TPB][SEL_MAX_G];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * SEL_WAVES + wave;
-    const bool active = t < T;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int64_t tb = (int64_t)blockIdx.x * tpb;
+    const int ntok = T - tb < tpb ? (int)(T - tb) : tpb;
     const int gsize = E / n_group;
+    const int64_t stride = T * E;
 
-    if (active) {
-        // four experts per lane at a time, partials read four splits at a time, so that
-        // 16 loads are in flight; each logit still adds its partials in split order
-        for (int eb = lane; eb < E; eb += 256) {
+    // each logit adds its partials in split order; at least eight loads are in flight:
+    // eight splits of one logit when there are many splits, else four logits per thread
+    const int nlog = ntok * E;
+    auto finish = [&](int i, double l64) {
+        const int tt = i / E, e = i - tt * E;
+        const float l = (float)l64;
+        if (logits_out) logits_out[(tb + tt) * E + e] = l;
+        const float sc = (float)(1.0 / (1.0 + exp(-(double)l)));
+        s_sc[tt][e] = sc;
+        s_sb[tt][e] = sc + bias[e];
+    };
+    if (nsplit >= 8) {
+        for (int i = tid; i < nlog; i += SEL_THREADS) {
+            const double* pe = part + tb * E + i;
+            double l64 = 0.0;
+            int sp = 0;
+            for (; sp + 8 <= nsplit; sp += 8) {
+                double v[8];
+#pragma unroll
+                for (int a = 0; a < 8; ++a) v[a] = pe[(int64_t)(sp + a) * stride];
+#pragma unroll
+                for (int a = 0; a < 8; ++a) l64 += v[a];
+            }
+            for (; sp < nsplit; ++sp) l64 += pe[(int64_t)sp * stride];
+            finish(i, l64);
+        }
+    } else {
+        for (int i0 = tid; i0 < nlog; i0 += 4 * SEL_THREADS) {
+            const double* pe[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * SEL_THREADS < nlog ? i0 + u * SEL_THREADS : i0;  // repeats stay in bounds
+                pe[u] = part + tb * E + i;
+            }
             double l64[4] = {0.0, 0.0, 0.0, 0.0};
             int sp = 0;
-            for (; sp + 4 <= nsplit; sp += 4) {
-                double v[4][4];
+            for (; sp + 2 <= nsplit; sp += 2) {
+                double v[2][4];
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+                for (int a = 0; a < 2; ++a)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int e = eb + 64 * u < E ? eb + 64 * u : E - 1;
-                        v[a][u] = part[((int64_t)(sp + a) * T + t) * E + e];
-                    }
+                    for (int u = 0; u < 4; ++u) v[a][u] = pe[u][(int64_t)(sp + a) * stride];
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+                for (int a = 0; a < 2; ++a)
 #pragma unroll
                     for (int u = 0; u < 4; ++u) l64[u] += v[a][u];
             }
             for (; sp < nsplit; ++sp)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = eb + 64 * u < E ? eb + 64 * u : E - 1;
-                    l64[u] += part[((int64_t)sp * T + t) * E + e];
-                }
+                for (int u = 0; u < 4; ++u) l64[u] += pe[u][(int64_t)sp * stride];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int e = eb + 64 * u;
-                if (e >= E) break;
-                const float l = (float)l64[u];
-                if (logits_out) logits_out[t * E + e] = l;
-                float sc = (float)(1.0 / (1.0 + exp(-(double)l)));
-                s_sc[wave][e] = sc;
-                s_sb[wave][e] = sc + bias[e];
+                const int i = i0 + u * SEL_THREADS;
+                if (i >= nlog) break;
+                finish(i, l64[u]);
             }
         }
     }
     __syncthreads();
-    if (active) {
-        for (int g = lane; g < n_group; g += 64) {
-            float a1 = -INFINITY, a2 = -INFINITY;
-            for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
-                float v = s_sb[wave][e];
-                if (v > a1) {
-                    a2 = a1;
-                    a1 = v;
-                } else if (v > a2) {
-                    a2 = v;
-                }
+    for (int i = tid; i < ntok * n_group; i += SEL_THREADS) {
+        const int tt = i / n_group, g = i - tt * n_group;
+        float a1 = -INFINITY, a2 = -INFINITY;
+        for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
+            const float v = s_sb[tt][e];
+            if (v > a1) {
+                a2 = a1;
+                a1 = v;
+            } else if (v > a2) {
+                a2 = v;
             }
-            s_gs[wave][g] = gsize >= 2 ? a1 + a2 : a1;
         }
+        s_gs[tt][g] = gsize >= 2 ? a1 + a2 : a1;
     }
     __syncthreads();
-    if (active) {
-        for (int g = lane; g < n_group; g += 64) {
-            float v = s_gs[wave][g];
-            int rank = 0;
-            for (int o = 0; o < n_group; ++o) rank += (o != g && ranks_before(s_gs[wave][o], o, v, g)) ? 1 : 0;
-            s_kept[wave][g] = rank < topk_group;
-        }
+    for (int i = tid; i < ntok * n_group; i += SEL_THREADS) {
+        const int tt = i / n_group, g = i - tt * n_group;
+        const float v = s_gs[tt][g];
+        int rank = 0;
+        for (int o = 0; o < n_group; ++o) rank += (o != g && ranks_before(s_gs[tt][o], o, v, g)) ? 1 : 0;
+        s_kept[tt][g] = rank < topk_group;
     }
     __syncthreads();
-    if (!active) return;
+    const int tt = tid >> 6;  // this wave's token
+    if (tt >= ntok) return;
+    const int64_t t = tb + tt;
 
     // lane owns experts lane, lane+64, ...; `taken` marks its chosen ones
     uint32_t taken = 0;
@@ -276,16 +298,16 @@ __global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const dou
         float bv = -INFINITY;
         int bi = 0x7fffffff;
         for (int q = 0, e = lane; e < E; ++q, e += 64) {
-            if (((taken >> q) & 1u) || !s_kept[wave][e / gsize]) continue;
-            float v = s_sb[wave][e];
+            if (((taken >> q) & 1u) || !s_kept[tt][e / gsize]) continue;
+            const float v = s_sb[tt][e];
             if (ranks_before(v, e, bv, bi)) {
                 bv = v;
                 bi = e;
             }
         }
         for (int off = 32; off >= 1; off >>= 1) {
-            float ov = __shfl_xor(bv, off);
-            int oi = __shfl_xor(bi, off);
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
             if (ranks_before(ov, oi, bv, bi)) {
                 bv = ov;
                 bi = oi;
@@ -294,7 +316,7 @@ __global__ void __launch_bounds__(SEL_WAVES * 64) router_select_kernel(const dou
         // non-finite scores compare false everywhere; keep the index in range regardless
         if (bi < 0 || bi >= E) bi = 0;
         if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        float sc = s_sc[wave][bi];
+        const float sc = s_sc[tt][bi];
         ssum += sc;
         if (lane == j) {
             my_e = bi;
@@ -311,9 +333,10 @@ hipError_t launch_router_select(const double* part, int nsplit, const float* bia
                                 int topk_group, int top_k, float rho, int32_t* idx, float* w, float* logits_out,
                                 hipStream_t s) {
     if (T == 0) return hipSuccess;
-    unsigned blocks = (unsigned)((T + SEL_WAVES - 1) / SEL_WAVES);
-    router_select_kernel<<<blocks, SEL_WAVES * 64, 0, s>>>(part, nsplit, bias, T, E, n_group, topk_group, top_k, rho,
-                                                          idx, w, logits_out);
+    const int tpb = T >= 1024 ? SEL_MAX_TPB : 1;  // small batches: more work-groups for the reduction
+    const unsigned blocks = (unsigned)((T + tpb - 1) / tpb);
+    router_select_kernel<<<blocks, SEL_THREADS, 0, s>>>(part, nsplit, bias, T, E, n_group, topk_group, top_k, rho, tpb,
+                                                       idx, w, logits_out);
     return hipGetLastError();
 }
 
