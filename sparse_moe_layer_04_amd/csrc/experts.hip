@@ -671,11 +671,20 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
             }
         }
     };
+    // row-block variants: 13..18 cover prefill-sized experts without padding blocks
     const int nrb = (te.row_count + 15) >> 4;
-    if (nrb > 16)
+    if (nrb > 17)
         run(std::integral_constant<int, 18>());
-    else if (nrb > 12)
+    else if (nrb > 16)
+        run(std::integral_constant<int, 17>());
+    else if (nrb > 15)
         run(std::integral_constant<int, 16>());
+    else if (nrb > 14)
+        run(std::integral_constant<int, 15>());
+    else if (nrb > 13)
+        run(std::integral_constant<int, 14>());
+    else if (nrb > 12)
+        run(std::integral_constant<int, 13>());
     else if (nrb > 8)
         run(std::integral_constant<int, 12>());
     else if (nrb > 4)
