@@ -24,9 +24,9 @@ namespace beam {
 //
 // Work item: (tile, column block).  A tile is up to GROWS = 288 consecutive rows of the
 // expert-sorted pair list, all routed to one expert (row_count may be smaller; 16-row
-// blocks past it are skipped).  A column block is 128 h columns (gate/up: 8 waves x
-// (16 gate + 16 up weight rows)) or 256 output columns (down: 8 waves x 32 weight
-// rows).  Each wave owns its weight rows: they stream from HBM straight into
+// blocks past it are skipped).  A column block is WAVES x 16 h columns (gate/up: each
+// wave 16 gate + 16 up weight rows) or WAVES x 32 output columns (down: 32 weight rows
+// per wave).  Each wave owns its weight rows: they stream from HBM straight into
 // registers, never through LDS.  All waves share the tile's activation rows
 // through an LDS double buffer.  K is swept 32 at a time; global loads of both
 // operands run 3 steps ahead in a ring of 4 register sets (one VMEM counter orders
@@ -35,8 +35,6 @@ namespace beam {
 constexpr int GROWS = 288;    // rows per tile: at 8192 tokens almost every expert fits one tile
 constexpr int GRB = GROWS / 16;
 constexpr int GKS = 32;       // k per step (one MFMA)
-constexpr int GWAVES = 8;
-constexpr int GTHREADS = GWAVES * 64;
 constexpr int GRING = 4;      // register sets: 3 steps in flight + 1 in use
 
 // LDS element offset of 16-byte chunk `ch` (0..3) of activation row `row` (64-byte rows).
@@ -77,19 +75,19 @@ __device__ __forceinline__ const uint16_t* act_row(const TileCtx& c, int row) {
 // a step the loads are issued activations first, then weights, so waiting for the
 // staged activations never waits for the newest weight loads.  Every load and store is
 // unconditional (clamped addresses): the steady state has no branches and the
-// compiler's memory-counter waits stay exact.  Thread t stages chunk (t + 512 i) mod
-// (NRB*64), so smaller variants reload cached chunks instead of branching.
-template <bool GATED, int NRB, int RING>
+// compiler's memory-counter waits stay exact.  Thread t stages chunk (t + THREADS i)
+// mod (NRB*64), so smaller variants reload cached chunks instead of branching.
+template <bool GATED, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROWS * GKS], f32x4 (&acc)[NRB][2]) {
     constexpr int ACH = NRB * 64;                          // 16-byte activation chunks per step
-    constexpr int AL = (ACH + GTHREADS - 1) / GTHREADS;    // activation loads per thread per step
+    constexpr int AL = (ACH + THREADS - 1) / THREADS;      // activation loads per thread per step
     const int lane = threadIdx.x & 63;
     const int tid = threadIdx.x;
     const uint16_t* ap[AL];
     int alds[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-        const int q = (tid + i * GTHREADS) % ACH;
+        const int q = (tid + i * THREADS) % ACH;
         const int row = q >> 2, ch = q & 3;
         ap[i] = act_row(c, row) + ch * 8;
         alds[i] = a_off(row, ch);
@@ -183,12 +181,12 @@ constexpr int SKS = SKC / 64;       // steps per chunk
 // LDS element offset of 16-byte chunk `ch` (0..SKC/8-1) of activation row `row`
 __device__ __forceinline__ int s_off(int row, int ch) { return row * SKC + ((ch ^ (row & 15)) << 3); }
 
-template <bool GATED, int NRB, int RING>
+template <bool GATED, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
     constexpr int ROWS = NRB * 16;
     constexpr int ACH = ROWS * SKC / 8;          // 16-byte chunks per activation chunk
-    constexpr int AL = ACH / GTHREADS;           // per thread
-    static_assert(AL * GTHREADS == ACH, "activation chunk split");
+    constexpr int AL = ACH / THREADS;            // per thread
+    static_assert(AL * THREADS == ACH, "activation chunk split");
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int nk = c.K / 64;                     // steps
     const int nchunk = c.K / SKC;
@@ -197,7 +195,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     int alds[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-        const int q = tid + i * GTHREADS;
+        const int q = tid + i * THREADS;
         const int row = q / (SKC / 8), ch = q % (SKC / 8);
         ap[i] = act_row(c, row) + ch * 8;
         alds[i] = s_off(row, ch);
@@ -270,7 +268,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 }
 
 // Runs one tile: main loop variant, then the epilogue.
-template <bool GATED, int NRB, int RING>
+template <bool GATED, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
     const int lane = threadIdx.x & 63;
     f32x4 acc[NRB][2];
@@ -278,11 +276,11 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (NRB <= 2) {
         if (c.K % SKC == 0)
-            tile_body_stream<GATED, NRB, RING>(c, &lds[0][0], acc);
+            tile_body_stream<GATED, NRB, RING, THREADS>(c, &lds[0][0], acc);
         else
-            tile_body<GATED, NRB, RING>(c, lds, acc);
+            tile_body<GATED, NRB, RING, THREADS>(c, lds, acc);
     } else
-        tile_body<GATED, NRB, RING>(c, lds, acc);
+        tile_body<GATED, NRB, RING, THREADS>(c, lds, acc);
 
     // ---- epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15) ----
 #pragma unroll
@@ -304,8 +302,9 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     }
 }
 
-template <bool GATED>
-__global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
+template <bool GATED, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                  const uint16_t* __restrict__ B0,
                                                                  const uint16_t* __restrict__ B1, int K, int N,
                                                                  int top_k, const int32_t* __restrict__ sorted_pairs,
@@ -344,12 +343,12 @@ __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t*
     // weight rows of this wave (two 16-row MFMA operand blocks)
     int col0;
     if (GATED) {
-        col0 = cblk * (GWAVES * 16) + wave * 16;
+        col0 = cblk * (WAVES * 16) + wave * 16;
         const int64_t r = (int64_t)e * N + col0 + (lane & 15);
         c.bp0 = B0 + r * K + (lane >> 4) * 8;
         c.bp1 = B1 + r * K + (lane >> 4) * 8;
     } else {
-        col0 = cblk * (GWAVES * 32) + wave * 32;
+        col0 = cblk * (WAVES * 32) + wave * 32;
         const int64_t r = (int64_t)e * N + col0 + (lane & 15);
         c.bp0 = B0 + r * K + (lane >> 4) * 8;
         c.bp1 = c.bp0 + (int64_t)16 * K;
@@ -363,20 +362,21 @@ __global__ void __launch_bounds__(GTHREADS) moe_gemm_bf16_kernel(const uint16_t*
     // row-count variants; small tiles are load-latency bound and keep 7 steps in flight
     const int nrb = (te.row_count + 15) >> 4;
 
+    constexpr int TH = WAVES * 64;
     if (nrb > 16)
-        run_tile<GATED, 18, 4>(c, lds);
+        run_tile<GATED, 18, 4, TH>(c, lds);
     else if (nrb > 12)
-        run_tile<GATED, 16, 4>(c, lds);
+        run_tile<GATED, 16, 4, TH>(c, lds);
     else if (nrb > 8)
-        run_tile<GATED, 12, 4>(c, lds);
+        run_tile<GATED, 12, 4, TH>(c, lds);
     else if (nrb > 4)
-        run_tile<GATED, 8, 4>(c, lds);
+        run_tile<GATED, 8, 4, TH>(c, lds);
     else if (nrb > 2)
-        run_tile<GATED, 4, 4>(c, lds);
+        run_tile<GATED, 4, 4, TH>(c, lds);
     else if (nrb > 1)
-        run_tile<GATED, 2, 4>(c, lds);
+        run_tile<GATED, 2, 4, TH>(c, lds);
     else
-        run_tile<GATED, 1, 4>(c, lds);
+        run_tile<GATED, 1, 4, TH>(c, lds);
 }
 
 // ---------------------------------------------------------------------------------
@@ -710,20 +710,29 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 // Average rows per expert from which the wide kernel is used (below it the weight
 // stream dominates and the 8-wave kernel's decode variant is faster).
 constexpr int64_t WIDE_MIN_ROWS_PER_EXPERT = 64;
+#ifndef DECODE_WAVES
+#define DECODE_WAVES 4
+#endif
 
 template <bool GATED>
 static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint16_t* B0, const uint16_t* B1, int K, int N,
                         int top_k, int64_t P, int E, const int32_t* sorted_pairs, const TileEntry* tiles,
                         const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C, hipStream_t s) {
-    const int ncols = GATED ? GWAVES * 16 : GWAVES * 32;  // same column blocks in both kernels
-    const int ncb = N / ncols;
-    const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-    if (P >= WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0)
+    if (P >= WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0) {
+        const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
+        const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
         moe_gemm_line_kernel<GATED, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
             A, (uint32_t)a_bytes, B0, B1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
-    else
-        moe_gemm_bf16_kernel<GATED><<<(unsigned)blocks, GTHREADS, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs,
-                                                                         tiles, num_tiles, ncb, C);
+    } else {
+        // decode-sized: 4-wave work-groups (two per compute unit) over half-width column
+        // blocks, so one work-group's start and end overlap another's weight stream and
+        // the last round of work items is shorter
+        constexpr int W = DECODE_WAVES;
+        const int ncb = N / (GATED ? W * 16 : W * 32);
+        const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
+        moe_gemm_bf16_kernel<GATED, W><<<(unsigned)blocks, W * 64, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs,
+                                                                          tiles, num_tiles, ncb, C);
+    }
 }
 
 hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int64_t T, int H, int I,
