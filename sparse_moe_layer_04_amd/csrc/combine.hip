@@ -14,7 +14,8 @@
 
 namespace beam {
 
-constexpr int CMB_THREADS = 256;
+constexpr int CMB_THREADS = 256;      // fp32 path
+constexpr int CMB_MAX_THREADS = 1024;  // bf16 path: about two 16-byte chunks per thread
 constexpr int CMB_MAX_K = 32;
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -28,10 +29,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return s;
 }
 
-// bf16 path: 8 consecutive features per step (16-byte loads).  With POST the summed
-// row is kept in LDS (H floats) for the post-norm pass.
+// bf16 path: 8 consecutive features per step (16-byte loads), one work-group per token
+// sized so that every thread takes about two chunks.  With POST the summed row is kept
+// in LDS (H floats) for the post-norm pass.
 template <bool POST>
-__global__ void __launch_bounds__(CMB_THREADS) combine_bf16_kernel(const uint16_t* __restrict__ y_pair,
+__global__ void __launch_bounds__(CMB_MAX_THREADS) combine_bf16_kernel(const uint16_t* __restrict__ y_pair,
                                                                    const float* __restrict__ topk_w, int H, int K,
                                                                    const uint16_t* __restrict__ x,
                                                                    const float* __restrict__ g2, float eps,
@@ -40,14 +42,15 @@ __global__ void __launch_bounds__(CMB_THREADS) combine_bf16_kernel(const uint16_
                                                                    uint16_t* __restrict__ moe_y) {
     extern __shared__ float ys[];
     __shared__ float wk[CMB_MAX_K];
-    __shared__ float red[CMB_THREADS / 64];
+    __shared__ float red[CMB_MAX_THREADS / 64];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nth = blockDim.x;
     if (tid < K) wk[tid] = topk_w[t * K + tid];
     __syncthreads();
     const int nch = H / 8;
     float ss = 0.f;
-    for (int c = tid; c < nch; c += CMB_THREADS) {
+    for (int c = tid; c < nch; c += nth) {
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.f;
@@ -77,7 +80,7 @@ __global__ void __launch_bounds__(CMB_THREADS) combine_bf16_kernel(const uint16_
     if (!POST) return;
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int c = tid; c < nch; c += CMB_THREADS) {
+    for (int c = tid; c < nch; c += nth) {
         const u32x4 xv = *(const u32x4*)(x + t * H + c * 8);
         float o[8];
 #pragma unroll
@@ -109,16 +112,19 @@ hipError_t launch_combine(const void* y_pair, bool bf16, const float* topk_w, in
                           const float* post_gain, float eps, float residual_k, void* out, void* moe_y,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
+    int nth = (H / 8 + 1) / 2;  // two 16-byte chunks per thread
+    nth = (nth + 63) / 64 * 64;
+    nth = nth < 64 ? 64 : (nth > CMB_MAX_THREADS ? CMB_MAX_THREADS : nth);
     if (!bf16) {
         combine_f32_kernel<<<(unsigned)T, CMB_THREADS, 0, s>>>((const float*)y_pair, topk_w, H, K, (float*)out);
     } else if (post_gain == nullptr) {
-        combine_bf16_kernel<false><<<(unsigned)T, CMB_THREADS, 0, s>>>(
+        combine_bf16_kernel<false><<<(unsigned)T, nth, 0, s>>>(
             (const uint16_t*)y_pair, topk_w, H, K, nullptr, nullptr, 0.f, 0.f, 0.f, (uint16_t*)out, nullptr);
     } else {
         const double k = (double)residual_k;
         const float cx = (float)sqrt((k - 1.0) / k);
         const float cy = (float)(1.0 / sqrt(k));
-        combine_bf16_kernel<true><<<(unsigned)T, CMB_THREADS, (size_t)H * sizeof(float), s>>>(
+        combine_bf16_kernel<true><<<(unsigned)T, nth, (size_t)H * sizeof(float), s>>>(
             (const uint16_t*)y_pair, topk_w, H, K, (const uint16_t*)x, post_gain, eps, cx, cy, (uint16_t*)out,
             (uint16_t*)moe_y);
     }
