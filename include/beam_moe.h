@@ -121,8 +121,9 @@ beam_status beam_moe_workspace_size(const beam_moe_shape* shape, int32_t op, siz
  *   r_t = fp32(1 / sqrt(mean_h x[t,h]^2 + eps))   (mean square accumulated in fp64,
  *                                                   r rounded once to fp32)
  *   u[t,h] = bf16_rne(fp32(fp32(x[t,h] * r_t) * gain[h]))
- * x, u: [T,H] bf16 (u may not alias x); gain [H] fp32.  shape->dtype must be
- * BEAM_BF16; only T and H are read.  Bitwise reproducible given x, gain, eps.
+ * x, u: [T,H] bf16, 16-byte aligned (u may not alias x); gain [H] fp32.
+ * shape->dtype must be BEAM_BF16 and H % 8 == 0 (else BEAM_ERR_UNSUPPORTED); only T
+ * and H are read.  Bitwise reproducible given x, gain, eps.
  */
 beam_status beam_moe_rmsnorm(const beam_moe_shape* shape, const void* x, const float* gain, float eps, void* u,
                              void* stream);

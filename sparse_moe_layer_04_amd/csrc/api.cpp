@@ -124,8 +124,8 @@ beam_status beam_moe_rmsnorm(const beam_moe_shape* shape, const void* x, const f
                              void* stream) {
     if (!shape || !x || !gain || !u || shape->T < 0 || shape->H < 1 || !(eps >= 0.f) || !isfinite(eps))
         return BEAM_ERR_INVALID_ARG;
-    if (shape->dtype != BEAM_BF16) return BEAM_ERR_UNSUPPORTED;
-    if (x == u) return BEAM_ERR_INVALID_ARG;
+    if (shape->dtype != BEAM_BF16 || shape->H % 8 != 0) return BEAM_ERR_UNSUPPORTED;
+    if (x == u || !aligned16(x) || !aligned16(u)) return BEAM_ERR_INVALID_ARG;
     if (shape->T == 0) return BEAM_OK;
     return hip_status(beam::launch_rmsnorm(static_cast<const uint16_t*>(x), gain, eps, shape->T, shape->H,
                                            static_cast<uint16_t*>(u), static_cast<hipStream_t>(stream)));

@@ -138,37 +138,56 @@ hipError_t launch_combine(const void* y_pair, bool bf16, const float* topk_w, in
 // rounded, so u does not depend on the summation order except in the last fp64 bit
 // of ss.
 // ---------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) rmsnorm_pinned_kernel(const uint16_t* __restrict__ x,
-                                                             const float* __restrict__ gain, float eps, int H,
-                                                             uint16_t* __restrict__ u) {
-    __shared__ double red[256];
+__global__ void __launch_bounds__(CMB_MAX_THREADS) rmsnorm_pinned_kernel(const uint16_t* __restrict__ x,
+                                                                         const float* __restrict__ gain, float eps,
+                                                                         int H, uint16_t* __restrict__ u) {
+    __shared__ double red[CMB_MAX_THREADS / 64];
     __shared__ float r_sh;
     const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
     const uint16_t* xr = x + t * H;
+    const int nch = H / 8;  // 16-byte chunks (H % 8 == 0 is checked by the caller)
     double ss = 0.0;
-    for (int h = threadIdx.x; h < H; h += 256) {
-        const double v = (double)bf16_to_f32(xr[h]);
-        ss += v * v;
+    for (int c = tid; c < nch; c += nth) {
+        const u32x4 v = *(const u32x4*)(xr + c * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double lo = (double)__uint_as_float(v[q] << 16);
+            const double hi = (double)__uint_as_float(v[q] & 0xFFFF0000u);
+            ss += lo * lo;
+            ss += hi * hi;
+        }
     }
-    red[threadIdx.x] = ss;
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    for (int n = 128; n >= 1; n >>= 1) {
-        if ((int)threadIdx.x < n) red[threadIdx.x] += red[threadIdx.x + n];
-        __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < nth / 64; ++w) tot += red[w];
+        r_sh = (float)(1.0 / sqrt(tot / (double)H + (double)eps));
     }
-    if (threadIdx.x == 0) r_sh = (float)(1.0 / sqrt(red[0] / (double)H + (double)eps));
     __syncthreads();
     const float r = r_sh;
-    for (int h = threadIdx.x; h < H; h += 256) {
-        const float a = __fmul_rn(bf16_to_f32(xr[h]), r);
-        u[t * H + h] = f32_to_bf16(__fmul_rn(a, gain[h]));
+    for (int c = tid; c < nch; c += nth) {
+        const u32x4 v = *(const u32x4*)(xr + c * 8);
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a0 = __fmul_rn(__uint_as_float(v[q] << 16), r);
+            const float a1 = __fmul_rn(__uint_as_float(v[q] & 0xFFFF0000u), r);
+            o[q] = pack_bf16x2(__fmul_rn(a0, gain[c * 8 + 2 * q]), __fmul_rn(a1, gain[c * 8 + 2 * q + 1]));
+        }
+        *(u32x4*)(u + t * H + c * 8) = o;
     }
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, int64_t T, int H, uint16_t* u,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
-    rmsnorm_pinned_kernel<<<(unsigned)T, 256, 0, s>>>(x, gain, eps, H, u);
+    int nth = (H / 8 + 1) / 2;  // two 16-byte chunks per thread
+    nth = (nth + 63) / 64 * 64;
+    nth = nth < 64 ? 64 : (nth > CMB_MAX_THREADS ? CMB_MAX_THREADS : nth);
+    rmsnorm_pinned_kernel<<<(unsigned)T, nth, 0, s>>>(x, gain, eps, H, u);
     return hipGetLastError();
 }
 

@@ -138,6 +138,10 @@ def test_route_permute_rmsnorm_validation():
         bm.BEAM_ERR_INVALID_ARG
     assert L.beam_moe_rmsnorm(ctypes.byref(s), FAKE, FAKE, ctypes.c_float(-1.0), FAKE + 64, None) == \
         bm.BEAM_ERR_INVALID_ARG
+    assert L.beam_moe_rmsnorm(ctypes.byref(s), FAKE, FAKE, ctypes.c_float(1e-6), FAKE + 72, None) == \
+        bm.BEAM_ERR_INVALID_ARG  # misaligned output
+    assert L.beam_moe_rmsnorm(ctypes.byref(_beam(H=100)), FAKE, FAKE, ctypes.c_float(1e-6), FAKE + 64, None) == \
+        bm.BEAM_ERR_UNSUPPORTED  # rows are read in 16-byte chunks
     assert L.beam_moe_rmsnorm(ctypes.byref(s0), FAKE, FAKE, ctypes.c_float(1e-6), FAKE + 64, None) == bm.BEAM_OK
 
 
