@@ -121,7 +121,8 @@ MID_CASES = {
     "mid_t1": mid_config("mid_t1", 1, seed_base=13000),
     "mid_skew_t700": mid_config("mid_skew_t700", 700, bias="zipf:0.6", seed_base=14000),
     "mid_sublayer_t333": mid_config("mid_sublayer_t333", 333, bias="zero", sublayer=True, seed_base=15000),
-    "mid_dense_t2500": mid_config("mid_dense_t2500", 2500, seed_base=17000),  # ~312 rows per expert: split tiles
+    "mid_dense_t2503": mid_config("mid_dense_t2503", 2503, seed_base=17000),  # ~313 rows per expert: split tiles;
+    # T >= 1024 and not a multiple of 4: the selection's last 4-token work-group is partial
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }
