@@ -123,6 +123,9 @@ MID_CASES = {
     "mid_sublayer_t333": mid_config("mid_sublayer_t333", 333, bias="zero", sublayer=True, seed_base=15000),
     "mid_dense_t2503": mid_config("mid_dense_t2503", 2503, seed_base=17000),  # ~313 rows per expert: split tiles;
     # T >= 1024 and not a multiple of 4: the selection's last 4-token work-group is partial
+    # the largest routing shape the ABI takes: E = 1024 experts in 64 groups, top-32
+    "mid_maxshape_t200": mid_config("mid_maxshape_t200", 200, H=256, E=1024, I=128, n_group=64, topk_group=8,
+                                    top_k=32, wr_std=math.sqrt(1.0 / 256), seed_base=18000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }
