@@ -7,6 +7,7 @@ line is the 8192-token prefill layer; the same run also times the 64-token decod
 (``secondary``).  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prefill_t8192]
+  python bench.py --sweep 16,64,256,1024 [--sweep-md table.md]   # serving shapes, one line per size
   python bench.py --copy-calib 1024      # plain 1 GiB device copy (HBM counter calibration)
   python bench.py --workload W --ingest-pmc FETCH.csv WRITE.csv CALIB_FETCH.csv CALIB_WRITE.csv 1024
 """
@@ -227,6 +228,30 @@ def cpu_baseline(cfg, hw, n_tokens):
                 n_tokens, cfg.name, " + norms" if cfg.sublayer else "", dt)}
 
 
+def sweep(base, hw, dw, sizes, steps, warmup, md_path=""):
+    """The layer at several token counts with the decode workload's input distributions
+    (serving shapes between decode and prefill); one JSON line per size."""
+    rows = []
+    for T in sizes:
+        c = base.replace(name="serve_t%d" % T, T=T)
+        r = run_workload(c, hw, dw, steps, warmup)
+        s = summarize(c, r, steps, warmup)
+        row = {"workload": c.name, "T": T, "tokens_per_s": s["tokens_per_s"], "ms_per_step": s["ms_per_step"],
+               "gate_up_ms": s["stages_ms"]["gate_up"], "down_ms": s["stages_ms"]["down"],
+               "experts_touched": s["experts_touched"], "rows_per_expert": T * c.top_k / c.E,
+               "mfma_frac": s["layer"]["mfma_frac"], "hbm_frac": s["layer"]["hbm_frac"]}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    if md_path:
+        with open(md_path, "w") as f:
+            f.write("| T | rows/expert | experts touched | ms / layer | tokens/s | gate/up ms | down ms | "
+                    "MFMA % | HBM % |\n|---|---|---|---|---|---|---|---|---|\n")
+            for r in rows:
+                f.write("| %d | %.1f | %d | %.3f | %.0f | %.3f | %.3f | %.1f | %.1f |\n" % (
+                    r["T"], r["rows_per_expert"], r["experts_touched"], r["ms_per_step"], r["tokens_per_s"],
+                    r["gate_up_ms"], r["down_ms"], 100 * r["mfma_frac"], 100 * r["hbm_frac"]))
+
+
 def copy_calibration(mib):
     import torch
     n = mib * 2 ** 20
@@ -249,6 +274,10 @@ def main():
     ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default="", metavar="T1,T2,...",
+                    help="time the layer on the decode workload's inputs at each token count (serving shapes) "
+                         "and print one JSON line per size instead of the benchmark line")
+    ap.add_argument("--sweep-md", default="", metavar="PATH", help="also write the sweep as a markdown table")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB")
     ap.add_argument("--ingest-pmc", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV",
                                                       "CALIB_MIB"),
@@ -286,6 +315,11 @@ def main():
     dw = tuple(dev(a) for a in hw)
     torch.cuda.synchronize()
     log("weights uploaded")
+
+    if args.sweep:
+        sweep(CONFIGS["decode_t64"], hw, dw, [int(t) for t in args.sweep.split(",")], args.steps, args.warmup,
+              args.sweep_md)
+        return
 
     prim = run_workload(cfg, hw, dw, args.steps, args.warmup)
     s = summarize(cfg, prim, args.steps, args.warmup)

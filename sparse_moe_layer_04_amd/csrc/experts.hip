@@ -707,9 +707,12 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
     return bf16 ? GROWS : (1 << 30);  // the fp32 path does not use tiles
 }
 
-// Average rows per expert from which the wide kernel is used (below it the weight
-// stream dominates and the 8-wave kernel's decode variant is faster).
-constexpr int64_t WIDE_MIN_ROWS_PER_EXPERT = 64;
+// Average rows per expert from which the line-streaming kernel is used.  Below it the
+// decode kernel (4-wave work-groups, two per CU) is 1-2% faster; above it the line kernel
+// wins, by 25% at 32-48 rows per expert (measured over 16..8192 tokens of the Beam layer).
+#ifndef WIDE_MIN_ROWS_PER_EXPERT
+#define WIDE_MIN_ROWS_PER_EXPERT 8
+#endif
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4
 #endif
@@ -718,7 +721,7 @@ template <bool GATED>
 static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint16_t* B0, const uint16_t* B1, int K, int N,
                         int top_k, int64_t P, int E, const int32_t* sorted_pairs, const TileEntry* tiles,
                         const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C, hipStream_t s) {
-    if (P >= WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0) {
+    if (P >= (int64_t)WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
         moe_gemm_line_kernel<GATED, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(

@@ -75,8 +75,13 @@ CONFIGS = {
     "skew_t6000": Config("skew_t6000", T=6000, bias="zipf:0.6", seed_base=3000, **_BEAM),
     "sublayer_t32768": Config("sublayer_t32768", T=32768, bias="zero", sublayer=True, residual_k=40,
                               seed_base=4000, **_BEAM),
+    # serving shapes between decode and prefill (the decode inputs at more tokens): 8 and 32
+    # routed rows per expert on average
+    "serve_t256": Config("serve_t256", T=256, bias="uniform:0.05", seed_base=5000, **_BEAM),
+    "serve_t1024": Config("serve_t1024", T=1024, bias="uniform:0.05", seed_base=6000, **_BEAM),
 }
-CONFIG_ORDER = ["tiny_f32", "decode_t64", "prefill_t8192", "skew_t6000", "sublayer_t32768"]
+CONFIG_ORDER = ["tiny_f32", "decode_t64", "prefill_t8192", "skew_t6000", "sublayer_t32768", "serve_t256",
+                "serve_t1024"]
 
 
 def seed_index(name: str) -> int:

@@ -126,6 +126,10 @@ MID_CASES = {
     # the largest routing shape the ABI takes: E = 1024 experts in 64 groups, top-32
     "mid_maxshape_t200": mid_config("mid_maxshape_t200", 200, H=256, E=1024, I=128, n_group=64, topk_group=8,
                                     top_k=32, wr_std=math.sqrt(1.0 / 256), seed_base=18000),
+    # 10 rows per expert: just above the kernel switch, the line kernel's smallest tiles
+    "mid_serve_t80": mid_config("mid_serve_t80", 80, seed_base=19000),
+    # 6 rows per expert on average but skewed: the decode kernel with tiles of up to T rows
+    "mid_skew_decode_t48": mid_config("mid_skew_decode_t48", 48, bias="zipf:0.6", seed_base=20000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }

@@ -1,5 +1,7 @@
 """GPU parity at the full Beam shapes (H=5120, E=256, I=2560; 20 GB of bf16 expert weights),
-in the launch configuration the benchmark times.
+in the launch configuration the benchmark times, and at two serving shapes between decode and
+prefill (256 and 1024 tokens: 8 and 32 routed rows per expert, on either side of the kernel
+switch).
 
 Routing is compared bit-exact (as sets) on ALL tokens; outputs are compared on a seeded
 sample of 256 tokens plus, for every non-empty expert, the tokens of its first and last
@@ -52,7 +54,8 @@ def _sample(cfg, idx, extra_cap=512):
     return np.union1d(base, ends)
 
 
-@pytest.mark.parametrize("name", ["decode_t64", "skew_t6000", "prefill_t8192", "sublayer_t32768"])
+@pytest.mark.parametrize("name", ["decode_t64", "serve_t256", "serve_t1024", "skew_t6000", "prefill_t8192",
+                                  "sublayer_t32768"])
 def test_full_shape_layer(name, weights):
     import torch
     import sparse_moe_layer_04_amd as bm
