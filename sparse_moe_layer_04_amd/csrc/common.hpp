@@ -26,14 +26,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// One grouped-GEMM work item: `row_count` consecutive rows of the expert-sorted
-// pair list starting at `row_begin`, all routed to `expert`.
+// One grouped-GEMM tile: `row_count` consecutive rows of the expert-sorted pair list
+// starting at `row_begin`, all routed to `expert`.  `group` = (j << 16) | n when the tile is
+// tile j of the n (< 32768) tiles of its expert, else 0.
 struct TileEntry {
     int32_t expert;
     int32_t row_begin;
     int32_t row_count;
-    int32_t pad;
+    int32_t group;
 };
+
+// Work item -> (tile, column block).  The items of an expert's tiles form one run of
+// n_tiles * n_col_blocks items ordered column block first, so the n tiles of an expert that
+// needs several read the same weight columns one after the other (from L2 for all but the
+// first); an expert of one tile keeps its column blocks in order.
+__device__ __forceinline__ void item_tile(const TileEntry* __restrict__ tiles, int item, int n_col_blocks, int& tile,
+                                          int& cblk) {
+    const int t0 = item / n_col_blocks;
+    const int grp = tiles[t0].group;
+    const int n = grp & 0xFFFF;
+    if (n > 1) {
+        const int first = t0 - (grp >> 16);
+        const int local = item - first * n_col_blocks;
+        cblk = local / n;
+        tile = first + local % n;
+    } else {
+        tile = t0;
+        cblk = item - t0 * n_col_blocks;
+    }
+}
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------------
 

@@ -324,8 +324,9 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
     if (slot >= per_xcd) return;
     const int item = (int)(blockIdx.x & 7) * per_xcd + slot;
     if (item >= work) return;
-    const TileEntry te = tiles[item / n_col_blocks];
-    const int cblk = item % n_col_blocks;
+    int tile, cblk;
+    item_tile(tiles, item, n_col_blocks, tile, cblk);
+    const TileEntry te = tiles[tile];
     if (te.row_count <= 0) return;
     const int e = te.expert;
 
@@ -598,8 +599,9 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     if (slot >= per_xcd) return;
     const int item = (int)(blockIdx.x & 7) * per_xcd + slot;
     if (item >= work) return;
-    const TileEntry te = tiles[item / n_col_blocks];
-    const int cblk = item % n_col_blocks;
+    int tile, cblk;
+    item_tile(tiles, item, n_col_blocks, tile, cblk);
+    const TileEntry te = tiles[tile];
     if (te.row_count <= 0) return;
     const int64_t e = te.expert;
     const int lane = threadIdx.x & 63;

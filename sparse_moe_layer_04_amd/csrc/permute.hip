@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ c
                     te.expert = k;
                     te.row_begin = off[k] + j * r;
                     te.row_count = (c - j * r) < r ? (c - j * r) : r;
-                    te.pad = 0;
+                    te.group = n < 32768 ? (j << 16) | n : 0;
                     tiles[toff[k] + j] = te;
                 }
             }
