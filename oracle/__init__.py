@@ -51,8 +51,10 @@ def _load():
         lib.oracle_rmsnorm_pinned.restype = None
         lib.oracle_route.argtypes = [vp, i32, i64, i64, vp, vp, i32, i32, i32, i32, f64, vp, vp, vp, vp, vp]
         lib.oracle_route.restype = ctypes.c_int
-        lib.oracle_experts.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i32, vp, vp, vp, i64, vp]
+        lib.oracle_experts.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i64, vp]
         lib.oracle_experts.restype = None
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_value.restype = f64
         lib.oracle_post_residual.argtypes = [vp, vp, i32, vp, f32, i64, i64, f64, vp]
         lib.oracle_post_residual.restype = None
         lib.oracle_threads.argtypes = []
@@ -126,23 +128,38 @@ def route(act: np.ndarray, w_router: np.ndarray, bias: np.ndarray, n_group: int,
     return Routing(idx, w, logits, margin, agree)
 
 
+def e4m3_value(code: int) -> float:
+    """The value of one OCP FP8 E4M3 code (the oracle's decoding)."""
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
 def experts(act: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, idx: np.ndarray,
-            w: np.ndarray, tokens: Optional[np.ndarray] = None) -> np.ndarray:
-    """y[n] = sum_j w[t,j] * SwiGLU-expert_{idx[t,j]}(act[t]) for t = tokens[n]; fp64 [n,H]."""
+            w: np.ndarray, tokens: Optional[np.ndarray] = None, w_scales=None) -> np.ndarray:
+    """y[n] = sum_j w[t,j] * SwiGLU-expert_{idx[t,j]}(act[t]) for t = tokens[n]; fp64 [n,H].
+
+    Weights are fp32, bf16 (uint16 bit patterns) or, with ``w_scales`` = (s_gate, s_up,
+    s_down), OCP FP8 E4M3 codes (uint8) with one E8M0 scale byte per 32 elements of a row."""
     act = _c(act)
     T, H = act.shape
     E, I, H2 = w_gate.shape
     assert H2 == H and w_up.shape == (E, I, H) and w_down.shape == (E, H, I)
-    wb = _is_bf16(w_gate)
-    assert _is_bf16(w_up) == wb and _is_bf16(w_down) == wb
+    if w_scales is not None:
+        assert w_gate.dtype == w_up.dtype == w_down.dtype == np.uint8
+        sg, su, sd = (np.ascontiguousarray(a, dtype=np.uint8) for a in w_scales)
+        assert sg.shape == (E, I, H // 32) and su.shape == (E, I, H // 32) and sd.shape == (E, H, I // 32)
+        fmt, sp = 2, (sg.ctypes.data, su.ctypes.data, sd.ctypes.data)
+    else:
+        fmt = _is_bf16(w_gate)
+        assert _is_bf16(w_up) == fmt and _is_bf16(w_down) == fmt
+        sp = (None, None, None)
     K = idx.shape[1]
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float64)
     tok = np.arange(T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
     y = np.empty((tok.size, H), dtype=np.float64)
     _load().oracle_experts(act.ctypes.data, _is_bf16(act), H, I, _c(w_gate).ctypes.data, _c(w_up).ctypes.data,
-                           _c(w_down).ctypes.data, wb, K, idx.ctypes.data, w.ctypes.data, tok.ctypes.data, tok.size,
-                           y.ctypes.data)
+                           _c(w_down).ctypes.data, fmt, sp[0], sp[1], sp[2], K, idx.ctypes.data, w.ctypes.data,
+                           tok.ctypes.data, tok.size, y.ctypes.data)
     return y
 
 
@@ -200,7 +217,7 @@ def layer(inp, tokens: Optional[np.ndarray] = None, want_logits: bool = False) -
     u = rmsnorm_pinned(inp.x, inp.pre_gain, cfg.eps) if cfg.sublayer else inp.x
     r = route(u, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, want_logits=want_logits)
     tok = np.arange(cfg.T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    y = experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, tok)
+    y = experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, tok, w_scales=inp.w_scales)
     out = post_residual(y, np.ascontiguousarray(inp.x[tok]), inp.post_gain, cfg.eps, cfg.residual_k) \
         if cfg.sublayer else y
     return LayerResult(u, r, tok, y, out)

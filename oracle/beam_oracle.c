@@ -73,6 +73,34 @@ static double elem(const void* p, int64_t i, int is_bf16) {
 
 static double sigmoid(double a) { return 1.0 / (1.0 + exp(-a)); }
 
+/* ---- 8-bit expert weights ------------------------------------------------------
+ * OCP FP8 E4M3: sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+ * holds the subnormals m * 2^-9; S.1111.111 is NaN (no infinities).  One E8M0 scale
+ * byte s per 32 consecutive elements of a row multiplies them by 2^(s - 127).
+ */
+double oracle_e4m3_value(uint8_t code) {
+    const int sgn = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* decoding tables for one call: value of every code and factor of every scale byte */
+typedef struct { double code[256], scale[256]; } fp8_tables;
+
+static void fp8_tables_init(fp8_tables* t) {
+    for (int i = 0; i < 256; ++i) {
+        t->code[i] = oracle_e4m3_value((uint8_t)i);
+        t->scale[i] = ldexp(1.0, i - 127);
+    }
+}
+
+/* weight element i stored as fp32 (fmt 0), bf16 (fmt 1) or E4M3 with block scales sc (fmt 2) */
+static double wval(const void* p, const uint8_t* sc, int64_t i, int fmt, const fp8_tables* t) {
+    if (fmt == 2) return t->code[((const uint8_t*)p)[i]] * t->scale[sc[i >> 5]];
+    return elem(p, i, fmt);
+}
+
 /* ---- pre-RMSNorm with the pinned fp32 rounding ------------------------------ */
 
 /* x [T,H] bf16, gain [H] fp32 -> u [T,H] bf16. */
@@ -240,12 +268,16 @@ int oracle_route(const void* act, int act_bf16, int64_t T, int64_t H, const floa
 /*
  * For each listed token tok[n] (n < n_tok): y[n, :] = sum_j wts[t,j] * FFN_{idx[t,j]}(act[t, :]),
  * j ascending, where FFN_e(u) = W_d[e] (silu(W_g[e] u) * (W_u[e] u)).
- * act [T,H]; w_gate, w_up [E,I,H]; w_down [E,H,I] (all fp32 or all bf16, per flags);
+ * act [T,H]; w_gate, w_up [E,I,H]; w_down [E,H,I], all stored as w_fmt: fp32 (0), bf16 (1)
+ * or E4M3 codes (2) with E8M0 block scales s_gate, s_up [E,I,H/32] and s_down [E,H,I/32];
  * idx [T,K]; wts [T,K] fp64.  y [n_tok,H] fp64.
  */
 void oracle_experts(const void* act, int act_bf16, int64_t H, int64_t I, const void* w_gate, const void* w_up,
-                    const void* w_down, int w_bf16, int K, const int32_t* idx, const double* wts,
-                    const int64_t* tok, int64_t n_tok, double* y) {
+                    const void* w_down, int w_fmt, const uint8_t* s_gate, const uint8_t* s_up,
+                    const uint8_t* s_down, int K, const int32_t* idx, const double* wts, const int64_t* tok,
+                    int64_t n_tok, double* y) {
+    fp8_tables tabs;
+    fp8_tables_init(&tabs);
 #pragma omp parallel
     {
         double* u = (double*)malloc(sizeof(double) * H);
@@ -263,15 +295,15 @@ void oracle_experts(const void* act, int act_bf16, int64_t H, int64_t I, const v
                     double a = 0.0, c = 0.0;
                     int64_t base = (e * I + i) * H;
                     for (int64_t h = 0; h < H; ++h) {
-                        a += elem(w_gate, base + h, w_bf16) * u[h];
-                        c += elem(w_up, base + h, w_bf16) * u[h];
+                        a += wval(w_gate, s_gate, base + h, w_fmt, &tabs) * u[h];
+                        c += wval(w_up, s_up, base + h, w_fmt, &tabs) * u[h];
                     }
                     hh[i] = a * sigmoid(a) * c;
                 }
                 for (int64_t o = 0; o < H; ++o) {
                     double z = 0.0;
                     int64_t base = (e * H + o) * I;
-                    for (int64_t i = 0; i < I; ++i) z += elem(w_down, base + i, w_bf16) * hh[i];
+                    for (int64_t i = 0; i < I; ++i) z += wval(w_down, s_down, base + i, w_fmt, &tabs) * hh[i];
                     yr[o] += wj * z;
                 }
             }

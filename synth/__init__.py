@@ -42,6 +42,8 @@ def _load():
             fn.restype = None
         lib.synth_words.argtypes = [u64, u64, u64, u64, vp]
         lib.synth_words.restype = None
+        lib.synth_quant_e4m3.argtypes = [vp, u64, u64, vp, vp]
+        lib.synth_quant_e4m3.restype = None
         _lib = lib
     return _lib
 
@@ -85,6 +87,20 @@ def subset(seed: int, tid: int, n: int, m: int) -> np.ndarray:
     if m >= n:
         return np.arange(n, dtype=np.int64)
     return np.sort(permutation(seed, tid, n)[:m])
+
+
+def quantize_e4m3(w: np.ndarray):
+    """bf16 weights [..., K] (uint16 bit patterns, K % 32 == 0) in 8-bit storage: OCP FP8
+    E4M3 codes [..., K] and E8M0 block scales [..., K/32] (uint8), as described in synth.c."""
+    if w.dtype != np.uint16 or w.shape[-1] % 32:
+        raise ValueError("expected bf16 bit patterns with a last dimension divisible by 32")
+    w = np.ascontiguousarray(w)
+    cols = w.shape[-1]
+    rows = w.size // cols
+    codes = np.empty(w.shape, dtype=np.uint8)
+    scales = np.empty(w.shape[:-1] + (cols // 32,), dtype=np.uint8)
+    _load().synth_quant_e4m3(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
 
 
 def bf16_to_f32(a: np.ndarray) -> np.ndarray:

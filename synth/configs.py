@@ -55,6 +55,8 @@ class Config:
     gain_std: float = 0.02
     seed_base: int = 0           # x-seed = seed_base + j
     weight_seed: Optional[int] = None  # None: same seed as x (config 0)
+    weights: str = "bf16"        # expert weight storage: "bf16", or "fp8" (E4M3 codes + E8M0 block
+                                 # scales from the bf16 draw, see synth.quantize_e4m3)
 
     @property
     def P(self) -> int:
@@ -105,6 +107,7 @@ class MoEInputs:
     w_down: np.ndarray       # [E,H,I]
     pre_gain: Optional[np.ndarray] = None   # [H] float32
     post_gain: Optional[np.ndarray] = None  # [H] float32
+    w_scales: Optional[tuple] = None        # fp8 weights: E8M0 scales of (w_gate, w_up, w_down)
 
 
 def _act(cfg: Config, seed: int, tid: int, shape, std: float, mean: float = 0.0):
@@ -112,6 +115,15 @@ def _act(cfg: Config, seed: int, tid: int, shape, std: float, mean: float = 0.0)
     if cfg.dtype == "bf16":
         return normal_bf16(seed, tid, shape, mean, std)
     return normal_f32(seed, tid, shape, mean, std)
+
+
+def fp8_weights(weights):
+    """(w_router, w_gate, w_up, w_down) with bf16 experts -> the same tuple with E4M3 expert
+    codes, and the (s_gate, s_up, s_down) E8M0 block scales."""
+    from . import quantize_e4m3
+    wr, wg, wu, wd = weights
+    (cg, sg), (cu, su), (cd, sd) = quantize_e4m3(wg), quantize_e4m3(wu), quantize_e4m3(wd)
+    return (wr, cg, cu, cd), (sg, su, sd)
 
 
 def expert_weights(cfg: Config, seed: Optional[int] = None):
@@ -143,14 +155,17 @@ def make_bias(cfg: Config, seed: int) -> np.ndarray:
     raise ValueError(kind)
 
 
-def make_inputs(cfg: Config, j: Optional[int] = None, weights=None) -> MoEInputs:
-    """All inputs of a config.  ``weights`` may pass a pre-generated (wr, wg, wu, wd) tuple."""
+def make_inputs(cfg: Config, j: Optional[int] = None, weights=None, w_scales=None) -> MoEInputs:
+    """All inputs of a config.  ``weights`` may pass a pre-generated (wr, wg, wu, wd) tuple
+    (for an fp8 config: the E4M3 codes, with their ``w_scales``)."""
     from . import normal_f32
     if j is None:
         j = seed_index(cfg.name)
     xs = cfg.seed_base + j
     if weights is None:
         weights = expert_weights(cfg, seed=(xs if cfg.weight_seed is None else cfg.weight_seed))
+        if cfg.weights == "fp8":
+            weights, w_scales = fp8_weights(weights)
     wr, wg, wu, wd = weights
     x = _act(cfg, xs, TID_X, (cfg.T, cfg.H), cfg.x_std)
     bias = make_bias(cfg, xs)
@@ -158,4 +173,4 @@ def make_inputs(cfg: Config, j: Optional[int] = None, weights=None) -> MoEInputs
     if cfg.sublayer:
         g1 = normal_f32(xs, TID_G1, (cfg.H,), 1.0, cfg.gain_std)
         g2 = normal_f32(xs, TID_G2, (cfg.H,), 1.0, cfg.gain_std)
-    return MoEInputs(cfg, xs, x, wr, bias, wg, wu, wd, g1, g2)
+    return MoEInputs(cfg, xs, x, wr, bias, wg, wu, wd, g1, g2, w_scales)

@@ -85,3 +85,61 @@ void synth_words(uint64_t seed, uint64_t tid, uint64_t first, uint64_t n, uint64
     uint64_t key = stream_key(seed, tid);
     for (uint64_t k = 0; k < n; ++k) out[k] = word_at(key, first + k);
 }
+
+/*
+ * Weights stored in 8 bits (an input format: how a weight tensor is handed to an FP8
+ * layer; no layer arithmetic).  OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent 0 is subnormal, m * 2^-9; no infinities; S.1111.111 is NaN;
+ * largest finite 448) with one E8M0 scale byte s per 32 consecutive elements of a row,
+ * meaning a factor 2^(s - 127).  Per block: s = 127 + ceil(log2(amax / 448)) (127 for an
+ * all-zero block), clamped to [1, 254]; each element w becomes the E4M3 value nearest to
+ * w / 2^(s - 127), ties to even mantissa.
+ */
+static uint8_t e4m3_nearest(double x) {
+    const uint8_t sign = x < 0 ? 0x80 : 0;
+    const double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (a < 0.015625) {                       /* below 2^-6: the subnormal grid m * 2^-9 */
+        const double m = nearbyint(a * 512.0);
+        return m >= 8.0 ? (uint8_t)(sign | 0x08) : (uint8_t)(sign | (uint8_t)m);
+    }
+    int e;
+    const double f = frexp(a, &e);            /* a = f * 2^e, f in [0.5, 1) */
+    int E = e + 6;                            /* a = (1 + m/8) * 2^(E - 7) */
+    double m = nearbyint((2.0 * f - 1.0) * 8.0);
+    if (m == 8.0) { m = 0.0; E += 1; }
+    if (E > 15 || (E == 15 && m > 6.0)) { E = 15; m = 6.0; }   /* 448; the block scale keeps |x| <= 448 */
+    return (uint8_t)(sign | (uint8_t)(E << 3) | (uint8_t)m);
+}
+
+static double bf16_bits_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* w [rows, cols] bf16 bit patterns (cols % 32 == 0) -> codes [rows, cols], scales [rows, cols/32] */
+void synth_quant_e4m3(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t* codes, uint8_t* scales) {
+    const int64_t nblk = (int64_t)(rows * (cols / 32));
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; ++b) {
+        const uint16_t* src = w + (uint64_t)b * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            const double v = fabs(bf16_bits_to_double(src[i]));
+            if (v > amax) amax = v;
+        }
+        int s = 127;
+        if (amax > 0.0) {
+            int e;
+            const double f = frexp(amax / 448.0, &e);
+            s = 127 + (f == 0.5 ? e - 1 : e);
+            if (s < 1) s = 1;
+            if (s > 254) s = 254;
+        }
+        scales[b] = (uint8_t)s;
+        const double inv = ldexp(1.0, 127 - s);
+        for (int i = 0; i < 32; ++i) codes[(uint64_t)b * 32 + i] = e4m3_nearest(bf16_bits_to_double(src[i]) * inv);
+    }
+}

@@ -27,8 +27,13 @@ MUTANTS = {
                              "return va > vb || (va == vb && a > b); }\nstatic int before_d"),
     "silu_on_up": ("hh[i] = a * sigmoid(a) * c;", "hh[i] = c * sigmoid(c) * a;"),
     "gelu_like_gate": ("hh[i] = a * sigmoid(a) * c;", "hh[i] = a * sigmoid(1.702 * a) * c;"),
-    "down_transposed": ("z += elem(w_down, base + i, w_bf16) * hh[i];",
-                        "z += elem(w_down, e * H * I + i * H + o, w_bf16) * hh[i];"),
+    "down_transposed": ("z += wval(w_down, s_down, base + i, w_fmt, &tabs) * hh[i];",
+                        "z += wval(w_down, s_down, e * H * I + i * H + o, w_fmt, &tabs) * hh[i];"),
+    "e4m3_exponent_bias_8": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_subnormal_as_normal": ("e == 0 ? ldexp((double)m, -9)", "e == 0 ? ldexp(1.0 + m / 8.0, -7)"),
+    "e4m3_mantissa_4_bits": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 16.0, e - 7)"),
+    "e8m0_scale_bias": ("t->scale[i] = ldexp(1.0, i - 127);", "t->scale[i] = ldexp(1.0, i - 128);"),
+    "scale_block_of_16": ("t->scale[sc[i >> 5]]", "t->scale[sc[i >> 4]]"),
     "weights_reversed": ("double wj = wts[t * K + j];", "double wj = wts[t * K + (K - 1 - j)];"),
     "rms_sum_not_mean": ("float r = (float)(1.0 / sqrt(ss / (double)H + (double)eps));",
                          "float r = (float)(1.0 / sqrt(ss + (double)eps));"),

@@ -11,7 +11,11 @@ Each test ties one oracle function to something other than itself:
   * RMSNorm: a hand-worked value, scale and gain laws, unit RMS, sign pattern;
   * the depth-scaled residual: the page's "sum divided by sqrt(k)" statement,
     the W_d = 0 and k = 1 cases;
-  * the parameter counts the pages print (three H x I matrices per expert).
+  * the parameter counts the pages print (three H x I matrices per expert);
+  * 8-bit expert weights: the E4M3 values the OCP FP8 format fixes (largest 448,
+    smallest normal 2^-6, subnormals m * 2^-9, NaN code), exact round trips of
+    representable blocks through the input quantizer, and the fp8 layer equal to the
+    layer on the decoded weights.
 Sources: Glonce "Reflection releases Beam, a 501B open MoE model with 1M context"
 (architecture paragraphs); transformers "Beam" model doc (Overview bullets "Sparse MoE"
 and "Sandwich norms with depth-scaled residuals", FP32 numerics paragraph).
@@ -405,3 +409,84 @@ def test_recorded_seeds_are_tie_free():
     inp = make_inputs(cfg, weights=(wr, None, None, None))
     r = oracle.route(inp.x, wr, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k)
     assert abs(r.min_margin() - seeds["min_margin"]["decode_t64"]) < 1e-15
+
+
+# ---- 8-bit (OCP FP8 E4M3 + E8M0 block scale) expert weights ----------------------
+
+def test_e4m3_values_fixed_by_the_format():
+    # OCP 8-bit floating point specification, E4M3: bias 7, largest finite 448 (S.1111.110),
+    # smallest normal 2^-6, largest subnormal 0.875 * 2^-6, smallest subnormal 2^-9,
+    # S.1111.111 is NaN, no infinities.
+    fixed = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x30: 0.5, 0x3C: 1.5, 0x7E: 448.0, 0x08: 2.0 ** -6,
+             0x07: 0.875 * 2.0 ** -6, 0x01: 2.0 ** -9, 0x04: 2.0 ** -7, 0xB8: -1.0, 0xFE: -448.0, 0x0F: 1.875 * 2.0 ** -6}
+    for code, v in fixed.items():
+        assert oracle.e4m3_value(code) == v, hex(code)
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    assert math.copysign(1.0, oracle.e4m3_value(0x80)) < 0 and oracle.e4m3_value(0x80) == 0.0
+    pos = [oracle.e4m3_value(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:]))                         # 127 increasing values
+    assert all(oracle.e4m3_value(0x80 | c) == -pos[c] for c in range(1, 0x7F))
+    # the normal binade [2^e, 2^(e+1)) holds 8 equally spaced values
+    for e in range(-6, 9):
+        vals = [v for v in pos if 2.0 ** e <= v < 2.0 ** (e + 1)]
+        assert len(vals) == (7 if e == 8 else 8) and vals[0] == 2.0 ** e
+        assert np.allclose(np.diff(vals), 2.0 ** (e - 3))
+
+
+def _representable_blocks(rows, cols, seed):
+    """bf16 weights whose every 32-element block is exactly E4M3 values times 2^(s-127),
+    with one element at 448 * 2^(s-127), so the block scale is s; returns (bf16, codes, s)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x7F, size=(rows, cols), dtype=np.uint8) | (rng.integers(0, 2, size=(rows, cols),
+                                                                                   dtype=np.uint8) << 7)
+    codes[codes == 0x80] = 0x00                                  # the quantizer writes +0 for zero
+    codes[:, ::32] = 0x7E | (codes[:, ::32] & 0x80)               # the block maximum
+    s = rng.integers(100, 130, size=(rows, cols // 32), dtype=np.uint8)
+    vals = np.array([oracle.e4m3_value(c) for c in range(256)])
+    w = vals[codes] * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    return synth.f32_to_bf16(w.astype(np.float32)), codes, s
+
+
+def test_quantizer_round_trips_representable_blocks():
+    w, codes, s = _representable_blocks(6, 128, 21)
+    assert (synth.bf16_to_f32(w).astype(np.float64) ==
+            np.array([oracle.e4m3_value(c) for c in range(256)])[codes] *
+            np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)).all()   # bf16 holds them exactly
+    c2, s2 = synth.quantize_e4m3(w)
+    assert (c2 == codes).all() and (s2 == s).all()
+
+
+def test_fp8_layer_equals_the_layer_on_the_decoded_weights():
+    # the fp8 path of the oracle against its bf16 path on weights that are exactly the
+    # decoded fp8 values (representable blocks: the two paths see identical numbers)
+    H, I, E, T = 64, 32, 4, 5
+    wg, cg, sg = _representable_blocks(E * I, H, 31)
+    wu, cu, su = _representable_blocks(E * I, H, 32)
+    wd, cd, sd = _representable_blocks(E * H, I, 33)
+    rng = np.random.default_rng(8)
+    u = synth.f32_to_bf16(rng.normal(size=(T, H)).astype(np.float32))
+    idx = rng.integers(0, E, size=(T, 2)).astype(np.int32)
+    wts = rng.uniform(0.1, 1.0, size=(T, 2))
+    y_bf16 = oracle.experts(u, wg.reshape(E, I, H), wu.reshape(E, I, H), wd.reshape(E, H, I), idx, wts)
+    y_fp8 = oracle.experts(u, cg.reshape(E, I, H), cu.reshape(E, I, H), cd.reshape(E, H, I), idx, wts,
+                           w_scales=(sg.reshape(E, I, H // 32), su.reshape(E, I, H // 32), sd.reshape(E, H, I // 32)))
+    assert (y_bf16 == y_fp8).all()
+    # and a swapped scale tensor is seen
+    y_bad = oracle.experts(u, cg.reshape(E, I, H), cu.reshape(E, I, H), cd.reshape(E, H, I), idx, wts,
+                           w_scales=(su.reshape(E, I, H // 32), sg.reshape(E, I, H // 32), sd.reshape(E, H, I // 32)))
+    assert not np.allclose(y_bad, y_fp8)
+
+
+def test_quantizer_error_bound_on_gaussian_weights():
+    # nearest-value rounding: |w - q| <= half the E4M3 spacing at q's binade times the scale
+    w = synth.normal_bf16(7, 3, (16, 256), 0.0, 0.02)
+    codes, s = synth.quantize_e4m3(w)
+    vals = np.array([oracle.e4m3_value(c) for c in range(256)])
+    q = vals[codes] * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    wf = synth.bf16_to_f32(w).astype(np.float64)
+    blk_max = np.abs(wf).reshape(16, 8, 32).max(axis=2).repeat(32, axis=1)
+    assert (np.abs(q).reshape(16, 8, 32).max(axis=2) <= 448 * np.ldexp(1.0, s.astype(np.int64) - 127)).all()
+    assert (blk_max <= 448 * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)).all()
+    spacing = np.maximum(np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(wf), 1e-30))).astype(np.int64) - 3),
+                         np.ldexp(1.0, s.astype(np.int64) - 127 - 9).repeat(32, axis=1))
+    assert (np.abs(wf - q) <= 0.5 * spacing * (1 + 1e-12)).all()
