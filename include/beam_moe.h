@@ -183,6 +183,30 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
                              void* out, int32_t* topk_idx, float* topk_w, void* moe_y, void* ws, size_t ws_bytes,
                              void* const* stage_events, void* stream);
 
+/*
+ * beam_moe_forward with 8-bit expert weights (bf16 activations; shape->dtype must be
+ * BEAM_BF16, else BEAM_ERR_UNSUPPORTED).  Each weight is stored as an OCP FP8 E4M3 code
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m * 2^-9; S.1111.111 is NaN; largest finite 448) and every 32 consecutive
+ * elements of a row along the reduction dimension share one E8M0 scale byte s, meaning
+ * 2^(s - 127); the weight is e4m3(code) * 2^(s - 127).
+ *   w_gate, w_up [E,I,H] and w_down [E,H,I]: E4M3 codes, one byte each, the layout of the
+ *            bf16 weights of beam_moe_forward (16-byte aligned)
+ *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes, s in 1..254, chosen
+ *            so that every decoded weight is a normal bf16 number (or zero)
+ * Every other argument, the workspace and the results are as for beam_moe_forward.  The
+ * weights are decoded to bf16 exactly (an E4M3 value times a power of two is a bf16
+ * value) and the layer then computes exactly what beam_moe_forward computes on the
+ * decoded weights; only the weight bytes read from memory halve.  This storage format is
+ * not on the Beam pages (they quote FP8 checkpoints without a scale scheme); it is the
+ * block-scaled layout of the OCP microscaling formats with 32-element blocks.
+ */
+beam_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
+                                 const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
+                                 const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down,
+                                 const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w, void* moe_y,
+                                 void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
+
 /* Static description of a status code. */
 const char* beam_status_string(beam_status status);
 

@@ -34,7 +34,7 @@ STAGE_NAMES = ("prenorm", "router_logits", "router_select", "permute", "gate_up"
 
 # exported C symbols (declared in include/beam_moe.h)
 EXPORTS = ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward",
-           "beam_status_string", "beam_moe_abi_version")
+           "beam_moe_forward_fp8", "beam_status_string", "beam_moe_abi_version")
 
 
 class Shape(ctypes.Structure):
@@ -55,7 +55,10 @@ _lib.beam_moe_route.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, 
 _lib.beam_moe_permute.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.beam_moe_forward.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Sublayer), _vp,
                                   _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
-for _f in ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward"):
+_lib.beam_moe_forward_fp8.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.POINTER(Sublayer), _vp, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
+for _f in ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward",
+           "beam_moe_forward_fp8"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.beam_status_string.argtypes = [ctypes.c_int]
 _lib.beam_status_string.restype = ctypes.c_char_p
@@ -138,16 +141,26 @@ def permute(shape: Shape, topk_idx, offsets, sorted_pairs, pair_pos, ws, stream=
 
 
 def forward(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, out, ws, sublayer: Optional[Sublayer] = None,
-            topk_idx=None, topk_w=None, moe_y=None, stage_events: Optional[Sequence[int]] = None, stream=None):
+            topk_idx=None, topk_w=None, moe_y=None, stage_events: Optional[Sequence[int]] = None, stream=None,
+            w_scales=None):
+    """beam_moe_forward; with ``w_scales`` = (s_gate, s_up, s_down) the expert weights are E4M3
+    codes (uint8) with E8M0 block scales and beam_moe_forward_fp8 is called."""
     ev = None
     if stage_events is not None:
         if len(stage_events) != NUM_STAGES + 1:
             raise ValueError("need %d stage events" % (NUM_STAGES + 1))
         ev = (_vp * (NUM_STAGES + 1))(*stage_events)
-    _check(_lib.beam_moe_forward(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate), _ptr(w_up),
-                                 _ptr(w_down), ctypes.byref(sublayer) if sublayer is not None else None, _ptr(out),
-                                 _ptr(topk_idx), _ptr(topk_w), _ptr(moe_y), _ptr(ws), _nbytes(ws), ev,
-                                 _stream(stream)), "beam_moe_forward")
+    sub = ctypes.byref(sublayer) if sublayer is not None else None
+    if w_scales is None:
+        _check(_lib.beam_moe_forward(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+                                     _ptr(w_up), _ptr(w_down), sub, _ptr(out), _ptr(topk_idx), _ptr(topk_w),
+                                     _ptr(moe_y), _ptr(ws), _nbytes(ws), ev, _stream(stream)), "beam_moe_forward")
+    else:
+        sg, su, sd = w_scales
+        _check(_lib.beam_moe_forward_fp8(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+                                         _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd), sub, _ptr(out),
+                                         _ptr(topk_idx), _ptr(topk_w), _ptr(moe_y), _ptr(ws), _nbytes(ws), ev,
+                                         _stream(stream)), "beam_moe_forward_fp8")
 
 
 def sublayer(pre_gain, post_gain, eps: float, residual_k: float) -> Sublayer:

@@ -163,18 +163,31 @@ beam_status beam_moe_permute(const beam_moe_shape* shape, const int32_t* topk_id
                                            pair_pos, nullptr, nullptr, 1, static_cast<hipStream_t>(stream)));
 }
 
-beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
-                             const void* w_gate, const void* w_up, const void* w_down, const beam_sublayer* sub,
-                             void* out, int32_t* topk_idx, float* topk_w, void* moe_y, void* ws, size_t ws_bytes,
-                             void* const* stage_events, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// E8M0 block scales of E4M3 expert weights (all three, or none for bf16/fp32 weights)
+struct WeightScales {
+    const uint8_t* gate;
+    const uint8_t* up;
+    const uint8_t* down;
+};
+
+beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
+                         const void* w_gate, const void* w_up, const void* w_down, const WeightScales* sc,
+                         const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w, void* moe_y, void* ws,
+                         size_t ws_bytes, void* const* stage_events, void* stream) {
     if (!shape_valid(shape) || !x || !w_router || !bias || !w_gate || !w_up || !w_down || !out)
         return BEAM_ERR_INVALID_ARG;
+    if (sc && (!sc->gate || !sc->up || !sc->down)) return BEAM_ERR_INVALID_ARG;
     if (sub && (!sub->pre_gain || !sub->post_gain || !(sub->eps > 0.f) || !isfinite(sub->eps) ||
                 !(sub->residual_k >= 1.f) || !isfinite(sub->residual_k)))
         return BEAM_ERR_INVALID_ARG;
     if (!shape_supported(shape)) return BEAM_ERR_UNSUPPORTED;
     const bool bf16 = shape->dtype == BEAM_BF16;
     if (sub && !bf16) return BEAM_ERR_UNSUPPORTED;
+    if (sc && !bf16) return BEAM_ERR_UNSUPPORTED;
     for (const void* p : {x, (const void*)w_router, w_gate, w_up, w_down, (const void*)out})
         if (!aligned16(p)) return BEAM_ERR_INVALID_ARG;
     if (moe_y && !aligned16(moe_y)) return BEAM_ERR_INVALID_ARG;
@@ -222,8 +235,8 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
     void* h = at<void>(ws, L.h);
     void* ypair = at<void>(ws, L.ypair);
     if (bf16) {
-        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, T, H, I, E, K, sorted, tiles, ntiles, L.max_tiles,
-                                      L.tile_rows, h, s));
+        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, sc ? sc->gate : nullptr, sc ? sc->up : nullptr, T, H,
+                                      I, E, K, sorted, tiles, ntiles, L.max_tiles, L.tile_rows, h, s));
     } else {
         BEAM_TRY(beam::launch_gate_up_f32(static_cast<const float*>(act), static_cast<const float*>(w_gate),
                                           static_cast<const float*>(w_up), H, I, K, sorted, idx, P,
@@ -231,8 +244,8 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
     }
     BEAM_TRY(mark(BEAM_STAGE_DOWN));
     if (bf16) {
-        BEAM_TRY(beam::launch_down(h, true, w_down, P, H, I, E, sorted, tiles, ntiles, L.max_tiles, L.tile_rows,
-                                   ypair, s));
+        BEAM_TRY(beam::launch_down(h, true, w_down, sc ? sc->down : nullptr, P, H, I, E, sorted, tiles, ntiles,
+                                   L.max_tiles, L.tile_rows, ypair, s));
     } else {
         BEAM_TRY(beam::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w_down), H, I, sorted,
                                        idx, P, static_cast<float*>(ypair), s));
@@ -243,6 +256,28 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
     BEAM_TRY(mark(BEAM_NUM_STAGES));
 #undef BEAM_TRY
     return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
+                             const void* w_gate, const void* w_up, const void* w_down, const beam_sublayer* sub,
+                             void* out, int32_t* topk_idx, float* topk_w, void* moe_y, void* ws, size_t ws_bytes,
+                             void* const* stage_events, void* stream) {
+    return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, nullptr, sub, out, topk_idx, topk_w, moe_y,
+                        ws, ws_bytes, stage_events, stream);
+}
+
+beam_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
+                                 const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
+                                 const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down,
+                                 const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w, void* moe_y,
+                                 void* ws, size_t ws_bytes, void* const* stage_events, void* stream) {
+    const WeightScales sc{s_gate, s_up, s_down};
+    return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, &sc, sub, out, topk_idx, topk_w, moe_y, ws,
+                        ws_bytes, stage_events, stream);
 }
 
 }  // extern "C"

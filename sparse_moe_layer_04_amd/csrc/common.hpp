@@ -91,14 +91,16 @@ inline int64_t max_tiles(int64_t P, int E, int tile_rows) { return (P + tile_row
 int gemm_tile_rows(int64_t P, int E, bool bf16);
 
 // h[row, :] = silu(A W_g^T) * (A W_u^T) for the expert-sorted rows (A = gathered token rows)
-// (act: T token rows; the activation and h tensors must stay below 4 GiB)
-hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int64_t T, int H, int I,
-                          int E, int top_k, const int32_t* sorted_pairs, const TileEntry* tiles,
-                          const int32_t* num_tiles, int64_t max_tile_count, int tile_rows, void* h, hipStream_t s);
+// (act: T token rows; the activation and h tensors must stay below 4 GiB).  With s_gate and
+// s_up the weights are E4M3 codes with E8M0 scales per 32 elements of a row (else bf16).
+hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, const uint8_t* s_gate,
+                          const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
+                          const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+                          int64_t max_tile_count, int tile_rows, void* h, hipStream_t s);
 
-// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T   (h: P rows)
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, int64_t P, int H, int I, int E,
-                       const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T   (h: P rows; E4M3 weights with s_down)
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, const uint8_t* s_down, int64_t P, int H, int I,
+                       int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s);
 
 // fp32 path (no tiles): one thread per output element

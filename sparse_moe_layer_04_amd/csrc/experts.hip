@@ -49,11 +49,32 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Per-tile context shared by the row-count variants of the main loop.
+// ---- 8-bit weights: OCP FP8 E4M3 codes with one E8M0 scale byte per 32 elements of a
+// row along K (the weight is e4m3(code) * 2^(scale - 127)).  An E4M3 value times a power of
+// two is exactly a bf16 value (3 mantissa bits, exponents in range), so the weights are
+// decoded exactly to bf16 in registers and the bf16 MFMA path is unchanged. ----
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// factor 2^(s - 127) of an E8M0 scale byte s (1..254)
+__device__ __forceinline__ float e8m0_factor(uint32_t s) { return __uint_as_float(s << 23); }
+
+// 8 E4M3 codes (dword lo holds codes 0..3, byte 0 first; hi codes 4..7) times `scale`
+__device__ __forceinline__ bf16x8 decode8(uint32_t lo, uint32_t hi, float scale) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Per-tile context shared by the row-count variants of the main loop.  Weight pointers
+// are byte pointers (2 bytes per bf16 weight, 1 per E4M3 code).
 struct TileCtx {
     const uint16_t* A;    // activations (gate/up: token rows, gathered) or h (down)
-    const uint16_t* bp0;  // this lane's first weight row (k offset applied)
-    const uint16_t* bp1;  // second weight row block (up rows, or the next 16 down rows)
+    const uint8_t* bp0;   // this lane's first weight row (k offset applied)
+    const uint8_t* bp1;   // second weight row block (up rows, or the next 16 down rows)
+    const uint8_t* sp0;   // E4M3: the scale rows of bp0's and bp1's rows
+    const uint8_t* sp1;
     int K, nk, top_k;     // reduction length, its 32-wide steps, routes per token
     bool gather;          // activation rows come from token rows via sorted_pairs
     int row_begin, row_count, ccol, N;
@@ -77,7 +98,7 @@ __device__ __forceinline__ const uint16_t* act_row(const TileCtx& c, int row) {
 // unconditional (clamped addresses): the steady state has no branches and the
 // compiler's memory-counter waits stay exact.  Thread t stages chunk (t + THREADS i)
 // mod (NRB*64), so smaller variants reload cached chunks instead of branching.
-template <bool GATED, int NRB, int RING, int THREADS>
+template <bool GATED, bool W8, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROWS * GKS], f32x4 (&acc)[NRB][2]) {
     constexpr int ACH = NRB * 64;                          // 16-byte activation chunks per step
     constexpr int AL = (ACH + THREADS - 1) / THREADS;      // activation loads per thread per step
@@ -94,6 +115,7 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     }
 
     u32x4 sa[AL], rb[RING][2];
+    uint32_t rs[RING][2];   // E4M3: the scale bytes of the step (one 32-k block)
     const int nk = c.nk;
     auto clampk = [&](int kstep) { return (kstep < nk ? kstep : nk - 1) * GKS; };
     auto load_a = [&](int kstep) {
@@ -103,8 +125,23 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     };
     auto load_b = [&](int kstep, int set) {
         const int k0 = clampk(kstep);
-        rb[set][0] = *(const u32x4*)(c.bp0 + k0);
-        rb[set][1] = *(const u32x4*)(c.bp1 + k0);
+        if constexpr (W8) {
+            const uint2 w0 = *(const uint2*)(c.bp0 + k0);
+            const uint2 w1 = *(const uint2*)(c.bp1 + k0);
+            rb[set][0] = u32x4{w0.x, w0.y, 0u, 0u};
+            rb[set][1] = u32x4{w1.x, w1.y, 0u, 0u};
+            rs[set][0] = c.sp0[k0 / 32];
+            rs[set][1] = c.sp1[k0 / 32];
+        } else {
+            rb[set][0] = *(const u32x4*)(c.bp0 + 2 * k0);
+            rb[set][1] = *(const u32x4*)(c.bp1 + 2 * k0);
+        }
+    };
+    auto wfrag = [&](int set, int blk) {
+        if constexpr (W8)
+            return decode8(rb[set][blk][0], rb[set][blk][1], e8m0_factor(rs[set][blk]));
+        else
+            return __builtin_bit_cast(bf16x8, rb[set][blk]);
     };
     auto store_a = [&](int buf) {
 #pragma unroll
@@ -114,8 +151,8 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     // fragment reads run LOOKAHEAD row blocks ahead of the MFMAs that use them
     constexpr int LOOKAHEAD = NRB < 4 ? NRB : 4;
     auto compute = [&](int set, int buf) {
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, rb[set][0]);
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, rb[set][1]);
+        const bf16x8 b0 = wfrag(set, 0);
+        const bf16x8 b1 = wfrag(set, 1);
         bf16x8 a[NRB];
 #pragma unroll
         for (int r = 0; r < LOOKAHEAD; ++r) a[r] = *(const bf16x8*)(&lds[buf][a_off(r * 16 + rd_row, rd_ch)]);
@@ -181,7 +218,7 @@ constexpr int SKS = SKC / 64;       // steps per chunk
 // LDS element offset of 16-byte chunk `ch` (0..SKC/8-1) of activation row `row`
 __device__ __forceinline__ int s_off(int row, int ch) { return row * SKC + ((ch ^ (row & 15)) << 3); }
 
-template <bool GATED, int NRB, int RING, int THREADS>
+template <bool GATED, bool W8, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
     constexpr int ROWS = NRB * 16;
     constexpr int ACH = ROWS * SKC / 8;          // 16-byte chunks per activation chunk
@@ -210,23 +247,40 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
         for (int i = 0; i < AL; ++i) *(u32x4*)(lds + buf * (ROWS * SKC) + alds[i]) = sa[i];
     };
-    // weights: lane's two chunks of each 128-byte window of its two 16-row blocks
-    const uint16_t* b0 = c.bp0 - (lane >> 4) * 8 + (lane >> 4) * 16;  // chunk 2*(lane>>4)
-    const uint16_t* b1 = c.bp1 - (lane >> 4) * 8 + (lane >> 4) * 16;
+    // weights: the lane's elements 16*(lane>>4) .. +15 of each 64-k step of its two 16-row
+    // blocks (bf16: the two 16-byte chunks 2*(lane>>4), 2*(lane>>4)+1 of a 128-byte window;
+    // E4M3: one 16-byte load)
+    constexpr int BPE = W8 ? 1 : 2;
+    const uint8_t* b0 = c.bp0 + ((lane >> 4) * 16 - (lane >> 4) * 8) * BPE;
+    const uint8_t* b1 = c.bp1 + ((lane >> 4) * 16 - (lane >> 4) * 8) * BPE;
     u32x4 rb[RING][4];
+    uint32_t rs[RING][2];   // E4M3: scale bytes of the lane's 32-k block
     auto load_b = [&](int kstep, int set) {
         const int k0 = (kstep < nk ? kstep : nk - 1) * 64;
-        rb[set][0] = *(const u32x4*)(b0 + k0);
-        rb[set][1] = *(const u32x4*)(b0 + k0 + 8);
-        rb[set][2] = *(const u32x4*)(b1 + k0);
-        rb[set][3] = *(const u32x4*)(b1 + k0 + 8);
+        if constexpr (W8) {
+            rb[set][0] = *(const u32x4*)(b0 + k0);
+            rb[set][2] = *(const u32x4*)(b1 + k0);
+            rs[set][0] = c.sp0[k0 / 32 + (lane >> 5)];
+            rs[set][1] = c.sp1[k0 / 32 + (lane >> 5)];
+        } else {
+            rb[set][0] = *(const u32x4*)(b0 + 2 * k0);
+            rb[set][1] = *(const u32x4*)(b0 + 2 * k0 + 16);
+            rb[set][2] = *(const u32x4*)(b1 + 2 * k0);
+            rb[set][3] = *(const u32x4*)(b1 + 2 * k0 + 16);
+        }
     };
     auto compute = [&](int kstep, int set, int buf) {
         const int w = (kstep % SKS) * 8;  // 16-byte chunk of the window inside the LDS chunk
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const bf16x8 g = __builtin_bit_cast(bf16x8, rb[set][h]);
-            const bf16x8 u = __builtin_bit_cast(bf16x8, rb[set][2 + h]);
+            bf16x8 g, u;
+            if constexpr (W8) {
+                g = decode8(rb[set][0][2 * h], rb[set][0][2 * h + 1], e8m0_factor(rs[set][0]));
+                u = decode8(rb[set][2][2 * h], rb[set][2][2 * h + 1], e8m0_factor(rs[set][1]));
+            } else {
+                g = __builtin_bit_cast(bf16x8, rb[set][h]);
+                u = __builtin_bit_cast(bf16x8, rb[set][2 + h]);
+            }
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
                 const bf16x8 a = *(const bf16x8*)(lds + buf * (ROWS * SKC) +
@@ -268,7 +322,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 }
 
 // Runs one tile: main loop variant, then the epilogue.
-template <bool GATED, int NRB, int RING, int THREADS>
+template <bool GATED, bool W8, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
     const int lane = threadIdx.x & 63;
     f32x4 acc[NRB][2];
@@ -276,11 +330,11 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (NRB <= 2) {
         if (c.K % SKC == 0)
-            tile_body_stream<GATED, NRB, RING, THREADS>(c, &lds[0][0], acc);
+            tile_body_stream<GATED, W8, NRB, RING, THREADS>(c, &lds[0][0], acc);
         else
-            tile_body<GATED, NRB, RING, THREADS>(c, lds, acc);
+            tile_body<GATED, W8, NRB, RING, THREADS>(c, lds, acc);
     } else
-        tile_body<GATED, NRB, RING, THREADS>(c, lds, acc);
+        tile_body<GATED, W8, NRB, RING, THREADS>(c, lds, acc);
 
     // ---- epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15) ----
 #pragma unroll
@@ -302,15 +356,12 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     }
 }
 
-template <bool GATED, int WAVES>
+template <bool GATED, bool W8, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
-moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                                 const uint16_t* __restrict__ B0,
-                                                                 const uint16_t* __restrict__ B1, int K, int N,
-                                                                 int top_k, const int32_t* __restrict__ sorted_pairs,
-                                                                 const TileEntry* __restrict__ tiles,
-                                                                 const int32_t* __restrict__ num_tiles,
-                                                                 int n_col_blocks, uint16_t* __restrict__ C) {
+moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B1,
+                     const uint8_t* __restrict__ S0, const uint8_t* __restrict__ S1, int K, int N, int top_k,
+                     const int32_t* __restrict__ sorted_pairs, const TileEntry* __restrict__ tiles,
+                     const int32_t* __restrict__ num_tiles, int n_col_blocks, uint16_t* __restrict__ C) {
     constexpr int LDS_ELEMS = 2 * GROWS * GKS > 2 * 32 * SKC ? 2 * GROWS * GKS : 2 * 32 * SKC;
     __shared__ __attribute__((aligned(16))) uint16_t lds_raw[LDS_ELEMS];
     auto lds = reinterpret_cast<uint16_t (*)[GROWS * GKS]>(lds_raw);
@@ -335,24 +386,34 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
     const int wave = tid >> 6;
 
     TileCtx c;
+    c.sp0 = c.sp1 = nullptr;
     c.nk = K / GKS;
     c.row_begin = te.row_begin;
     c.row_count = te.row_count;
     c.N = N;
     c.sorted_pairs = sorted_pairs;
     c.C = C;
-    // weight rows of this wave (two 16-row MFMA operand blocks)
+    // weight rows of this wave (two 16-row MFMA operand blocks); byte pointers
+    constexpr int BPE = W8 ? 1 : 2;
     int col0;
     if (GATED) {
         col0 = cblk * (WAVES * 16) + wave * 16;
         const int64_t r = (int64_t)e * N + col0 + (lane & 15);
-        c.bp0 = B0 + r * K + (lane >> 4) * 8;
-        c.bp1 = B1 + r * K + (lane >> 4) * 8;
+        c.bp0 = B0 + (r * K + (lane >> 4) * 8) * BPE;
+        c.bp1 = B1 + (r * K + (lane >> 4) * 8) * BPE;
+        if (W8) {
+            c.sp0 = S0 + r * (K / 32);
+            c.sp1 = S1 + r * (K / 32);
+        }
     } else {
         col0 = cblk * (WAVES * 32) + wave * 32;
         const int64_t r = (int64_t)e * N + col0 + (lane & 15);
-        c.bp0 = B0 + r * K + (lane >> 4) * 8;
-        c.bp1 = c.bp0 + (int64_t)16 * K;
+        c.bp0 = B0 + (r * K + (lane >> 4) * 8) * BPE;
+        c.bp1 = c.bp0 + (int64_t)16 * K * BPE;
+        if (W8) {
+            c.sp0 = S0 + r * (K / 32);
+            c.sp1 = c.sp0 + (int64_t)16 * (K / 32);
+        }
     }
     c.ccol = col0 + (lane & 15);
     c.A = A;
@@ -365,19 +426,19 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A,
 
     constexpr int TH = WAVES * 64;
     if (nrb > 16)
-        run_tile<GATED, 18, 4, TH>(c, lds);
+        run_tile<GATED, W8, 18, 4, TH>(c, lds);
     else if (nrb > 12)
-        run_tile<GATED, 16, 4, TH>(c, lds);
+        run_tile<GATED, W8, 16, 4, TH>(c, lds);
     else if (nrb > 8)
-        run_tile<GATED, 12, 4, TH>(c, lds);
+        run_tile<GATED, W8, 12, 4, TH>(c, lds);
     else if (nrb > 4)
-        run_tile<GATED, 8, 4, TH>(c, lds);
+        run_tile<GATED, W8, 8, 4, TH>(c, lds);
     else if (nrb > 2)
-        run_tile<GATED, 4, 4, TH>(c, lds);
+        run_tile<GATED, W8, 4, 4, TH>(c, lds);
     else if (nrb > 1)
-        run_tile<GATED, 2, 4, TH>(c, lds);
+        run_tile<GATED, W8, 2, 4, TH>(c, lds);
     else
-        run_tile<GATED, 1, 4, TH>(c, lds);
+        run_tile<GATED, W8, 1, 4, TH>(c, lds);
 }
 
 // ---------------------------------------------------------------------------------
@@ -421,38 +482,50 @@ struct LineCtx {
     __amdgpu_buffer_rsrc_t act;   // activation tensor (token rows or h rows)
     __amdgpu_buffer_rsrc_t w0;    // weight blocks [0, NB/2)
     __amdgpu_buffer_rsrc_t w1;    // weight blocks [NB/2, NB)
+    __amdgpu_buffer_rsrc_t s0;    // E4M3: scale rows of the blocks of w0
+    __amdgpu_buffer_rsrc_t s1;    //       and of w1
     uint32_t wvoff;               // this lane's byte offset inside a weight block
+    uint32_t svoff;               // E4M3: this lane's byte offset inside a block's scale rows
     int K, top_k, row_begin, row_count;
     bool gather;
     const int32_t* sorted_pairs;
 };
 
 // Weight loads of step `kstep` of a work item into ring slot `set` (steps past the end
-// reload the last step, which the cache still holds).
-template <int NB, int RING>
-__device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], int b, int kstep, int set) {
+// reload the last step, which the cache still holds).  bf16: two 16-byte chunks per block
+// (a whole 128-byte line per row); E4M3: one 16-byte load of the same 16 elements per lane
+// and the scale byte of their 32-k block.
+template <int NB, int RING, bool W8>
+__device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB],
+                                            int b, int kstep, int set) {
     constexpr int HB = NB / 2;
+    constexpr int BPE = W8 ? 1 : 2;
     const int nk = c.K / WKS;
-    const uint32_t so = (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2) + (uint32_t)(b % HB) * (uint32_t)(16 * c.K * 2);
+    const int ks = kstep < nk ? kstep : nk - 1;
+    const uint32_t so = (uint32_t)(ks * WKS * BPE) + (uint32_t)(b % HB) * (uint32_t)(16 * c.K * BPE);
     const __amdgpu_buffer_rsrc_t r = b < HB ? c.w0 : c.w1;
     rb[set][b][0] = buf_load(r, c.wvoff, so);
-    rb[set][b][1] = buf_load(r, c.wvoff + 16, so);
+    if constexpr (W8) {
+        const uint32_t ss = (uint32_t)(ks * (WKS / 32)) + (uint32_t)(b % HB) * (uint32_t)(16 * (c.K / 32));
+        rs[set][b] = __builtin_amdgcn_raw_buffer_load_b8(b < HB ? c.s0 : c.s1, c.svoff, ss, 0);
+    } else {
+        rb[set][b][1] = buf_load(r, c.wvoff + 16, so);
+    }
 }
 
-// The weights of a work item's first RING-1 steps (issued before the previous item's
-// epilogue, so the stream does not stop between items).
-template <int NB, int RING>
-__device__ __forceinline__ void line_prologue_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2]) {
+// The weights of a work item's first RING-1 steps.
+template <int NB, int RING, bool W8>
+__device__ __forceinline__ void line_prologue_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB]) {
 #pragma unroll
     for (int s2 = 0; s2 < RING - 1; ++s2)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) line_load_b<NB, RING>(c, rb, b, s2, s2);
+        for (int b = 0; b < NB; ++b) line_load_b<NB, RING, W8>(c, rb, rs, b, s2, s2);
 }
 
 // Main loop of one work item; the caller has issued its first RING-1 weight steps.
-template <int WAVES, int NB, int RING, int NRB>
+template <int WAVES, int NB, int RING, int NRB, bool W8>
 __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4 (&rb)[RING][NB][2],
-                                          f32x4 (&acc)[NRB][NB]) {
+                                          uint32_t (&rs)[RING][NB], f32x4 (&acc)[NRB][NB]) {
     constexpr int THREADS = WAVES * 64;
     constexpr int ACH = NRB * 16 * 8;                  // 16-byte activation chunks per step
     constexpr int AL = (ACH + THREADS - 1) / THREADS;
@@ -480,7 +553,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
     auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
     auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
-    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING>(c, rb, b, kstep, set); };
+    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, W8>(c, rb, rs, b, kstep, set); };
     // fragment read offsets: row r*16 + (lane & 15), chunks 2g and 2g+1 (g = lane >> 4)
     const int fr = lane & 15, g = lane >> 4;
     const int off_e = w_off(fr, 2 * g);
@@ -507,6 +580,19 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
         const uint16_t* L = lds + (j & 1) * WBUF_ELEMS;
         const int wbuf = (j + 1) & 1;
         lds_barrier();
+        // this step's weight fragments (E4M3: decoded exactly to bf16)
+        bf16x8 wf[NB][2];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if constexpr (W8) {
+                const float sc = e8m0_factor(rs[set][b]);
+                wf[b][0] = decode8(rb[set][b][0][0], rb[set][b][0][1], sc);
+                wf[b][1] = decode8(rb[set][b][0][2], rb[set][b][0][3], sc);
+            } else {
+                wf[b][0] = __builtin_bit_cast(bf16x8, rb[set][b][0]);
+                wf[b][1] = __builtin_bit_cast(bf16x8, rb[set][b][1]);
+            }
+        }
         bf16x8 ae[NRB], ao[NRB];
 #pragma unroll
         for (int r = 0; r < LA; ++r) {
@@ -522,10 +608,8 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const bf16x8 bw = __builtin_bit_cast(bf16x8, rb[set][b][0]);
-                acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae[r], bw, acc[r][b], 0, 0, 0);
-            }
+            for (int b = 0; b < NB; ++b)
+                acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae[r], wf[b][0], acc[r][b], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
             // this row block's share of the step's memory operations
 #pragma unroll
@@ -541,10 +625,8 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
                 }
             }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const bf16x8 bw = __builtin_bit_cast(bf16x8, rb[set][b][1]);
-                acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao[r], bw, acc[r][b], 0, 0, 0);
-            }
+            for (int b = 0; b < NB; ++b)
+                acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao[r], wf[b][1], acc[r][b], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
         }
     };
@@ -576,12 +658,12 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     }
 }
 
-template <bool GATED, int WAVES, int NB, int RING>
+template <bool GATED, bool W8, int WAVES, int NB, int RING>
 __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
-    const uint16_t* __restrict__ A, uint32_t a_bytes, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, int K, int N, int top_k, const int32_t* __restrict__ sorted_pairs,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_col_blocks,
-    uint16_t* __restrict__ C) {
+    const uint16_t* __restrict__ A, uint32_t a_bytes, const uint8_t* __restrict__ B0,
+    const uint8_t* __restrict__ B1, const uint8_t* __restrict__ S0, const uint8_t* __restrict__ S1, int K, int N,
+    int top_k, const int32_t* __restrict__ sorted_pairs, const TileEntry* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int n_col_blocks, uint16_t* __restrict__ C) {
     static_assert(WAVES * NB * 16 == 256 && NB % 2 == 0, "a work-group covers 256 weight rows");
     // the output tile is staged through LDS (rows padded by 16 bytes) once the main loop is done
     constexpr int EPI_COLS = GATED ? WAVES * (NB / 2) * 16 : WAVES * NB * 16;
@@ -615,29 +697,41 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     c.row_count = te.row_count;
     c.gather = GATED;
     c.sorted_pairs = sorted_pairs;
-    c.wvoff = (uint32_t)(((lane & 15) * K + (lane >> 4) * 16) * 2);
-    const uint32_t bytes = (uint32_t)(HB * 16 * K * 2);
+    constexpr int BPE = W8 ? 1 : 2;   // bytes per weight
+    c.wvoff = (uint32_t)(((lane & 15) * K + (lane >> 4) * 16) * BPE);
+    c.svoff = (uint32_t)((lane & 15) * (K / 32) + (lane >> 5));   // E4M3: block of elements 16*(lane>>4)
+    const uint32_t bytes = (uint32_t)(HB * 16 * K * BPE);
+    const uint32_t sbytes = (uint32_t)(HB * 16 * (K / 32));
     int col0;
+    int64_t r0, r1;   // first weight rows of the blocks of w0 and w1
     if (GATED) {
         col0 = cblk * (WAVES * HB * 16) + wave * (HB * 16);  // h columns [col0, col0 + 16*HB)
-        c.w0 = make_rsrc(B0 + (e * N + col0) * (int64_t)K, bytes);
-        c.w1 = make_rsrc(B1 + (e * N + col0) * (int64_t)K, bytes);
+        r0 = r1 = e * N + col0;
+        c.w0 = make_rsrc(B0 + r0 * K * BPE, bytes);
+        c.w1 = make_rsrc(B1 + r1 * K * BPE, bytes);
     } else {
         col0 = cblk * (WAVES * NB * 16) + wave * (NB * 16);  // output columns [col0, col0 + 16*NB)
-        c.w0 = make_rsrc(B0 + (e * N + col0) * (int64_t)K, bytes);
-        c.w1 = make_rsrc(B0 + (e * N + col0 + HB * 16) * (int64_t)K, bytes);
+        r0 = e * N + col0;
+        r1 = r0 + HB * 16;
+        c.w0 = make_rsrc(B0 + r0 * K * BPE, bytes);
+        c.w1 = make_rsrc(B0 + r1 * K * BPE, bytes);
+    }
+    if (W8) {
+        c.s0 = make_rsrc(S0 + r0 * (K / 32), sbytes);
+        c.s1 = make_rsrc((GATED ? S1 : S0) + r1 * (K / 32), sbytes);
     }
 
     auto run = [&](auto nrbc) {
         constexpr int NRB = decltype(nrbc)::value;
         u32x4 rb[RING][NB][2];
-        line_prologue_b<NB, RING>(c, rb);
+        uint32_t rs[RING][NB];
+        line_prologue_b<NB, RING, W8>(c, rb, rs);
         f32x4 acc[NRB][NB];
 #pragma unroll
         for (int r = 0; r < NRB; ++r)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        line_body<WAVES, NB, RING, NRB>(c, lds, rb, acc);
+        line_body<WAVES, NB, RING, NRB, W8>(c, lds, rb, rs, acc);
         // epilogue: each wave writes its bf16 columns of the tile into LDS (C layout of a
         // 16x16 block: rows 4*(lane>>4)+q, column lane&15), then the work-group stores
         // whole 16-byte chunks of every output row.  silu(g) = g / (1 + e^-g) with the
@@ -719,15 +813,16 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 #define DECODE_WAVES 4
 #endif
 
-template <bool GATED>
-static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint16_t* B0, const uint16_t* B1, int K, int N,
-                        int top_k, int64_t P, int E, const int32_t* sorted_pairs, const TileEntry* tiles,
-                        const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C, hipStream_t s) {
+template <bool GATED, bool W8>
+static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, const uint8_t* B1, const uint8_t* S0,
+                        const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, const int32_t* sorted_pairs,
+                        const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C,
+                        hipStream_t s) {
     if (P >= (int64_t)WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-        moe_gemm_line_kernel<GATED, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
-            A, (uint32_t)a_bytes, B0, B1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
+        moe_gemm_line_kernel<GATED, W8, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
+            A, (uint32_t)a_bytes, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
     } else {
         // decode-sized: 4-wave work-groups (two per compute unit) over half-width column
         // blocks, so one work-group's start and end overlap another's weight stream and
@@ -735,26 +830,39 @@ static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint16_t* B0,
         constexpr int W = DECODE_WAVES;
         const int ncb = N / (GATED ? W * 16 : W * 32);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-        moe_gemm_bf16_kernel<GATED, W><<<(unsigned)blocks, W * 64, 0, s>>>(A, B0, B1, K, N, top_k, sorted_pairs,
-                                                                          tiles, num_tiles, ncb, C);
+        moe_gemm_bf16_kernel<GATED, W8, W><<<(unsigned)blocks, W * 64, 0, s>>>(
+            A, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
     }
 }
 
-hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int64_t T, int H, int I,
-                          int E, int top_k, const int32_t* sorted_pairs, const TileEntry* tiles,
-                          const int32_t* num_tiles, int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
+hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, const uint8_t* s_gate,
+                          const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
+                          const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+                          int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
-    launch_gemm<true>((const uint16_t*)act, (uint64_t)T * H * 2, (const uint16_t*)w_gate, (const uint16_t*)w_up, H, I,
-                      top_k, T * top_k, E, sorted_pairs, tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
+    const uint16_t* A = (const uint16_t*)act;
+    const uint8_t *B0 = (const uint8_t*)w_gate, *B1 = (const uint8_t*)w_up;
+    if (s_gate)
+        launch_gemm<true, true>(A, (uint64_t)T * H * 2, B0, B1, s_gate, s_up, H, I, top_k, T * top_k, E, sorted_pairs,
+                                tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
+    else
+        launch_gemm<true, false>(A, (uint64_t)T * H * 2, B0, B1, nullptr, nullptr, H, I, top_k, T * top_k, E,
+                                 sorted_pairs, tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, int64_t P, int H, int I, int E,
-                       const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, const uint8_t* s_down, int64_t P, int H, int I,
+                       int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
-    launch_gemm<false>((const uint16_t*)h, (uint64_t)P * I * 2, (const uint16_t*)w_down, nullptr, I, H, 0, P, E,
-                       sorted_pairs, tiles, num_tiles, max_tile_count, (uint16_t*)y_pair, s);
+    const uint16_t* A = (const uint16_t*)h;
+    const uint8_t* B0 = (const uint8_t*)w_down;
+    if (s_down)
+        launch_gemm<false, true>(A, (uint64_t)P * I * 2, B0, nullptr, s_down, nullptr, I, H, 0, P, E, sorted_pairs,
+                                 tiles, num_tiles, max_tile_count, (uint16_t*)y_pair, s);
+    else
+        launch_gemm<false, false>(A, (uint64_t)P * I * 2, B0, nullptr, nullptr, nullptr, I, H, 0, P, E, sorted_pairs,
+                                  tiles, num_tiles, max_tile_count, (uint16_t*)y_pair, s);
     return hipGetLastError();
 }
 

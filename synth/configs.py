@@ -81,9 +81,13 @@ CONFIGS = {
     # routed rows per expert on average
     "serve_t256": Config("serve_t256", T=256, bias="uniform:0.05", seed_base=5000, **_BEAM),
     "serve_t1024": Config("serve_t1024", T=1024, bias="uniform:0.05", seed_base=6000, **_BEAM),
+    # the decode and prefill workloads with 8-bit expert weights (E4M3 codes + E8M0 scales per
+    # 32 elements, quantized from the same bf16 draw)
+    "decode_t64_fp8": Config("decode_t64_fp8", T=64, bias="uniform:0.05", seed_base=1000, weights="fp8", **_BEAM),
+    "prefill_t8192_fp8": Config("prefill_t8192_fp8", T=8192, bias="zero", seed_base=2000, weights="fp8", **_BEAM),
 }
 CONFIG_ORDER = ["tiny_f32", "decode_t64", "prefill_t8192", "skew_t6000", "sublayer_t32768", "serve_t256",
-                "serve_t1024"]
+                "serve_t1024", "decode_t64_fp8", "prefill_t8192_fp8"]
 
 
 def seed_index(name: str) -> int:

@@ -51,6 +51,7 @@ class DeviceInputs:
         self.wd = dev(inp.w_down)
         self.g1 = dev(inp.pre_gain) if inp.pre_gain is not None else None
         self.g2 = dev(inp.post_gain) if inp.post_gain is not None else None
+        self.w_scales = tuple(dev(a) for a in inp.w_scales) if inp.w_scales is not None else None
 
 
 def run_forward(cfg: Config, d: DeviceInputs, timer=None):
@@ -67,7 +68,7 @@ def run_forward(cfg: Config, d: DeviceInputs, timer=None):
     moe_y = torch.empty((cfg.T, cfg.H), dtype=act_dt, device="cuda") if cfg.sublayer else None
     sub = bm.sublayer(d.g1, d.g2, cfg.eps, cfg.residual_k) if cfg.sublayer else None
     bm.forward(shape, d.x, d.wr, d.bias, d.wg, d.wu, d.wd, out, ws, sublayer=sub, topk_idx=idx, topk_w=w,
-               moe_y=moe_y, stage_events=timer.events if timer else None)
+               moe_y=moe_y, stage_events=timer.events if timer else None, w_scales=d.w_scales)
     torch.cuda.synchronize()
     return dict(out=host(out), idx=host(idx), w=host(w), moe_y=host(moe_y) if moe_y is not None else None)
 
@@ -130,6 +131,14 @@ MID_CASES = {
     "mid_serve_t80": mid_config("mid_serve_t80", 80, seed_base=19000),
     # 6 rows per expert on average but skewed: the decode kernel with tiles of up to T rows
     "mid_skew_decode_t48": mid_config("mid_skew_decode_t48", 48, bias="zipf:0.6", seed_base=20000),
+    # 8-bit expert weights (E4M3 + E8M0 block scales): the line kernel, the decode kernel's
+    # 64-k stream (gate/up, K = 512) and 32-k steps (down, K = 256), and its large-tile loop
+    "mid_fp8_prefill_t1000": mid_config("mid_fp8_prefill_t1000", 1000, weights="fp8", seed_base=21000),
+    "mid_fp8_decode_t24": mid_config("mid_fp8_decode_t24", 24, weights="fp8", seed_base=22000),
+    "mid_fp8_skew_decode_t48": mid_config("mid_fp8_skew_decode_t48", 48, bias="zipf:0.6", weights="fp8",
+                                          seed_base=23000),
+    "mid_fp8_sublayer_t333": mid_config("mid_fp8_sublayer_t333", 333, sublayer=True, residual_k=40,
+                                        weights="fp8", seed_base=24000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }

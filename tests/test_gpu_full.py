@@ -1,7 +1,7 @@
 """GPU parity at the full Beam shapes (H=5120, E=256, I=2560; 20 GB of bf16 expert weights),
-in the launch configuration the benchmark times, and at two serving shapes between decode and
+in the launch configuration the benchmark times, at two serving shapes between decode and
 prefill (256 and 1024 tokens: 8 and 32 routed rows per expert, on either side of the kernel
-switch).
+switch), and for decode and prefill with the weights in 8-bit storage (E4M3 + E8M0 scales).
 
 Routing is compared bit-exact (as sets) on ALL tokens; outputs are compared on a seeded
 sample of 256 tokens plus, for every non-empty expert, the tokens of its first and last
@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from synth.configs import CONFIGS, expert_weights, make_inputs
+from synth.configs import CONFIGS, expert_weights, fp8_weights, make_inputs
 
 from moe_cases import as_f64, assert_routing_equal, dev, host, rel_err, shape_of
 
@@ -38,6 +38,22 @@ def weights():
     torch.cuda.empty_cache()
 
 
+@pytest.fixture(scope="module")
+def weights_fp8(weights):
+    """The same weights in 8-bit storage (E4M3 codes + E8M0 block scales)."""
+    import torch
+    hw, _ = weights
+    t0 = time.time()
+    hq, scales = fp8_weights(hw)
+    dq = tuple(dev(a) for a in hq)
+    ds = tuple(dev(a) for a in scales)
+    torch.cuda.synchronize()
+    print("\nfp8 weights: quantized and uploaded in %.1fs" % (time.time() - t0), flush=True)
+    yield hq, scales, dq, ds
+    del dq, ds
+    torch.cuda.empty_cache()
+
+
 def _sample(cfg, idx, extra_cap=512):
     T = cfg.T
     if T <= 512:
@@ -55,13 +71,17 @@ def _sample(cfg, idx, extra_cap=512):
 
 
 @pytest.mark.parametrize("name", ["decode_t64", "serve_t256", "serve_t1024", "skew_t6000", "prefill_t8192",
-                                  "sublayer_t32768"])
-def test_full_shape_layer(name, weights):
+                                  "sublayer_t32768", "decode_t64_fp8", "prefill_t8192_fp8"])
+def test_full_shape_layer(name, request):
     import torch
     import sparse_moe_layer_04_amd as bm
-    hw, dw = weights
     cfg = CONFIGS[name]
-    inp = make_inputs(cfg, weights=hw)
+    if cfg.weights == "fp8":
+        hw, w_scales, dw, d_scales = request.getfixturevalue("weights_fp8")
+    else:
+        hw, dw = request.getfixturevalue("weights")
+        w_scales = d_scales = None
+    inp = make_inputs(cfg, weights=hw, w_scales=w_scales)
     print("\n[%s] x-seed %d" % (name, inp.x_seed), flush=True)
     t0 = time.time()
     u = oracle.rmsnorm_pinned(inp.x, inp.pre_gain, cfg.eps) if cfg.sublayer else inp.x
@@ -83,7 +103,7 @@ def test_full_shape_layer(name, weights):
         g1, g2 = dev(inp.pre_gain), dev(inp.post_gain)
         sub = bm.sublayer(g1, g2, cfg.eps, cfg.residual_k)
     bm.forward(shape, x, dw[0], dev(inp.bias), dw[1], dw[2], dw[3], out, ws, sublayer=sub, topk_idx=idx, topk_w=w,
-               moe_y=moe_y)
+               moe_y=moe_y, w_scales=d_scales)
     torch.cuda.synchronize()
     g_idx, g_w = host(idx), host(w)
     assert_routing_equal(g_idx, g_w, r.idx, r.w, cfg.rho)
@@ -93,7 +113,7 @@ def test_full_shape_layer(name, weights):
 
     tok = _sample(cfg, r.idx)
     t0 = time.time()
-    y = oracle.experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, tok)
+    y = oracle.experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, tok, w_scales=inp.w_scales)
     ref = oracle.post_residual(y, np.ascontiguousarray(inp.x[tok]), inp.post_gain, cfg.eps, cfg.residual_k) \
         if cfg.sublayer else y
     print("[%s] oracle experts on %d tokens: %.1fs" % (name, tok.size, time.time() - t0), flush=True)
