@@ -39,22 +39,28 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def weight_bytes_per_element(cfg):
+    """bf16: 2; 8-bit storage: 1 byte per code plus one scale byte per 32 elements."""
+    return 1.0 + 1.0 / 32 if cfg.weights == "fp8" else 2.0
+
+
 def gate_up_work(cfg, n_touched):
     """Algorithmic flops and bytes of one gate/up launch.
 
     flops: 4*H*I per routed pair (gate and up products).
-    bytes: each touched expert's gate and up matrices once (2*I*H bf16), each token row
+    bytes: each touched expert's gate and up matrices once (2*I*H weights), each token row
     once (H bf16), each h row written once (I bf16)."""
     P = cfg.T * cfg.top_k
     flops = 4.0 * cfg.H * cfg.I * P
-    nbytes = n_touched * 2.0 * cfg.I * cfg.H * 2 + cfg.T * cfg.H * 2.0 + P * cfg.I * 2.0
+    nbytes = n_touched * 2.0 * cfg.I * cfg.H * weight_bytes_per_element(cfg) + cfg.T * cfg.H * 2.0 + P * cfg.I * 2.0
     return flops, nbytes
 
 
 def down_work(cfg, n_touched):
     """flops 2*H*I per pair; bytes: each touched W_d once, each h row read, each output row written."""
     P = cfg.T * cfg.top_k
-    return 2.0 * cfg.H * cfg.I * P, n_touched * cfg.H * cfg.I * 2.0 + P * (cfg.I + cfg.H) * 2.0
+    return (2.0 * cfg.H * cfg.I * P,
+            n_touched * cfg.H * cfg.I * weight_bytes_per_element(cfg) + P * (cfg.I + cfg.H) * 2.0)
 
 
 def roofline(flops, nbytes, seconds, traffic=None):
@@ -132,7 +138,9 @@ def ingest_counters(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write
     print(json.dumps({workload: ent}))
 
 
-def run_workload(cfg, hw, dw, steps, warmup):
+def run_workload(cfg, hw, dw, steps, warmup, scales=None):
+    """Times `steps` layers of workload `cfg` (weights hw on the host, dw on the device; for
+    8-bit weights `scales` = (host scales, device scales))."""
     import numpy as np
     import torch
 
@@ -144,7 +152,7 @@ def run_workload(cfg, hw, dw, steps, warmup):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    inp = make_inputs(cfg, weights=hw)
+    inp = make_inputs(cfg, weights=hw, w_scales=scales[0] if scales else None)
     shape = bm.make_shape(cfg.T, cfg.H, cfg.E, cfg.I, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, cfg.dtype)
     op = bm.OP_FORWARD_SUBLAYER if cfg.sublayer else bm.OP_FORWARD
     ws = torch.empty(bm.workspace_size(shape, op), dtype=torch.uint8, device="cuda")
@@ -159,7 +167,7 @@ def run_workload(cfg, hw, dw, steps, warmup):
 
     def step(timer=None):
         bm.forward(shape, x, dw[0], bias, dw[1], dw[2], dw[3], out, ws, sublayer=sub, topk_idx=idx,
-                   stage_events=timer.events if timer else None)
+                   stage_events=timer.events if timer else None, w_scales=scales[1] if scales else None)
 
     for _ in range(warmup):
         step()
@@ -190,7 +198,7 @@ def summarize(cfg, r, steps, warmup):
     gu_f, gu_b = gate_up_work(cfg, r["n_touched"])
     dn_f, dn_b = down_work(cfg, r["n_touched"])
     layer_flops = 6.0 * cfg.H * cfg.I * P
-    weight_bytes = r["n_touched"] * 3.0 * cfg.H * cfg.I * 2
+    weight_bytes = r["n_touched"] * 3.0 * cfg.H * cfg.I * weight_bytes_per_element(cfg)
     layer_bytes = weight_bytes + cfg.E * cfg.H * 4.0 + 2.0 * cfg.T * cfg.H * 2
     import sparse_moe_layer_04_amd as bm
     return {
@@ -274,6 +282,7 @@ def main():
     ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit-weight decode and prefill layers")
     ap.add_argument("--sweep", default="", metavar="T1,T2,...",
                     help="time the layer on the decode workload's inputs at each token count (serving shapes) "
                          "and print one JSON line per size instead of the benchmark line")
@@ -359,6 +368,25 @@ def main():
                              "experts_touched": s2["experts_touched"]}
     del dw
     torch.cuda.empty_cache()
+    if not args.no_fp8 and args.workload == "prefill_t8192":
+        # the same layers with the expert weights in 8-bit storage (E4M3 codes + E8M0 scales
+        # per 32 elements; beam_moe_forward_fp8), quantized from the same bf16 weights
+        from synth.configs import fp8_weights
+        hq, hs = fp8_weights(hw)
+        dq, ds = tuple(dev(a) for a in hq), tuple(dev(a) for a in hs)
+        torch.cuda.synchronize()
+        line["fp8_weights"] = {}
+        for name in ("decode_t64_fp8", "prefill_t8192_fp8"):
+            c8 = CONFIGS[name]
+            r8 = run_workload(c8, hq, dq, args.steps, args.warmup, scales=(hs, ds))
+            s8 = summarize(c8, r8, args.steps, args.warmup)
+            log("fp8 %s: %.3f ms/step" % (name, s8["ms_per_step"]))
+            line["fp8_weights"][name] = {"tokens_per_s": s8["tokens_per_s"], "ms_per_step": s8["ms_per_step"],
+                                         "layer": s8["layer"], "stages_ms": s8["stages_ms"],
+                                         "gate_up": s8["gate_up"], "down": s8["down"],
+                                         "experts_touched": s8["experts_touched"]}
+        del dq, ds, hq, hs
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, hw, args.cpu_tokens)
     print(json.dumps(line), flush=True)

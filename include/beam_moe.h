@@ -192,8 +192,8 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
  * 2^(s - 127); the weight is e4m3(code) * 2^(s - 127).
  *   w_gate, w_up [E,I,H] and w_down [E,H,I]: E4M3 codes, one byte each, the layout of the
  *            bf16 weights of beam_moe_forward (16-byte aligned)
- *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes, s in 1..254, chosen
- *            so that every decoded weight is a normal bf16 number (or zero)
+ *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes (16-byte aligned),
+ *            s in 1..254, chosen so that every decoded weight is a normal bf16 number (or zero)
  * Every other argument, the workspace and the results are as for beam_moe_forward.  The
  * weights are decoded to bf16 exactly (an E4M3 value times a power of two is a bf16
  * value) and the layer then computes exactly what beam_moe_forward computes on the

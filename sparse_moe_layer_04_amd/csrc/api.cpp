@@ -181,6 +181,7 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     if (!shape_valid(shape) || !x || !w_router || !bias || !w_gate || !w_up || !w_down || !out)
         return BEAM_ERR_INVALID_ARG;
     if (sc && (!sc->gate || !sc->up || !sc->down)) return BEAM_ERR_INVALID_ARG;
+    if (sc && (!aligned16(sc->gate) || !aligned16(sc->up) || !aligned16(sc->down))) return BEAM_ERR_INVALID_ARG;
     if (sub && (!sub->pre_gain || !sub->post_gain || !(sub->eps > 0.f) || !isfinite(sub->eps) ||
                 !(sub->residual_k >= 1.f) || !isfinite(sub->residual_k)))
         return BEAM_ERR_INVALID_ARG;

@@ -213,7 +213,6 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
 // of SKC columns for all rows of the tile (one barrier per chunk); the next chunk's
 // global loads are issued a whole chunk ahead.
 constexpr int SKC = 512;            // activation columns per LDS chunk
-constexpr int SKS = SKC / 64;       // steps per chunk
 
 // LDS element offset of 16-byte chunk `ch` (0..SKC/8-1) of activation row `row`
 __device__ __forceinline__ int s_off(int row, int ch) { return row * SKC + ((ch ^ (row & 15)) << 3); }
@@ -225,7 +224,12 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     constexpr int AL = ACH / THREADS;            // per thread
     static_assert(AL * THREADS == ACH, "activation chunk split");
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
-    const int nk = c.K / 64;                     // steps
+    // a step is 64 k for bf16 weights (one 128-byte line per row) and 128 k for E4M3 (one
+    // 128-byte line per row: two 16-byte loads per lane, 64 bytes apart)
+    constexpr int SW = W8 ? 128 : 64;
+    constexpr int SKS_ = SKC / SW;               // steps per activation chunk
+    static_assert(SKS_ % RING == 0, "ring slots are static inside a chunk");
+    const int nk = c.K / SW;                     // steps
     const int nchunk = c.K / SKC;
     // activation staging of this thread
     const uint16_t* ap[AL];
@@ -247,21 +251,20 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
         for (int i = 0; i < AL; ++i) *(u32x4*)(lds + buf * (ROWS * SKC) + alds[i]) = sa[i];
     };
-    // weights: the lane's elements 16*(lane>>4) .. +15 of each 64-k step of its two 16-row
-    // blocks (bf16: the two 16-byte chunks 2*(lane>>4), 2*(lane>>4)+1 of a 128-byte window;
-    // E4M3: one 16-byte load)
+    // weights: per 64 k, the lane's elements 16*(lane>>4) .. +15 of its two 16-row blocks
+    // (bf16: the 16-byte chunks 2*(lane>>4) and 2*(lane>>4)+1 of the row's 128-byte window;
+    // E4M3: one 16-byte load, and a second one for the step's other 64 k)
     constexpr int BPE = W8 ? 1 : 2;
     const uint8_t* b0 = c.bp0 + ((lane >> 4) * 16 - (lane >> 4) * 8) * BPE;
     const uint8_t* b1 = c.bp1 + ((lane >> 4) * 16 - (lane >> 4) * 8) * BPE;
     u32x4 rb[RING][4];
-    uint32_t rs[RING][2];   // E4M3: scale bytes of the lane's 32-k block
     auto load_b = [&](int kstep, int set) {
-        const int k0 = (kstep < nk ? kstep : nk - 1) * 64;
+        const int k0 = (kstep < nk ? kstep : nk - 1) * SW;
         if constexpr (W8) {
             rb[set][0] = *(const u32x4*)(b0 + k0);
+            rb[set][1] = *(const u32x4*)(b0 + k0 + 64);
             rb[set][2] = *(const u32x4*)(b1 + k0);
-            rs[set][0] = c.sp0[k0 / 32 + (lane >> 5)];
-            rs[set][1] = c.sp1[k0 / 32 + (lane >> 5)];
+            rb[set][3] = *(const u32x4*)(b1 + k0 + 64);
         } else {
             rb[set][0] = *(const u32x4*)(b0 + 2 * k0);
             rb[set][1] = *(const u32x4*)(b0 + 2 * k0 + 16);
@@ -269,14 +272,31 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
             rb[set][3] = *(const u32x4*)(b1 + 2 * k0 + 16);
         }
     };
+    // E4M3 scales: the 16 scale bytes of an activation chunk (4 steps x 4 blocks of 32 k) of
+    // each of the lane's two rows, one 16-byte load per row and chunk, one chunk ahead; byte
+    // 4j + 2l + (lane>>5) scales load l (0, 1) of step j of the chunk
+    u32x4 sc[2] = {}, scn[2] = {};
+    auto load_s = [&](int chunk) {
+        if constexpr (W8) {
+            const int ck = chunk < nchunk ? chunk : nchunk - 1;
+            scn[0] = *(const u32x4*)(c.sp0 + ck * 16);
+            scn[1] = *(const u32x4*)(c.sp1 + ck * 16);
+        }
+    };
+    auto scale_of = [&](int blk, int j, int l) {
+        return e8m0_factor((sc[blk][j] >> (8 * (2 * l + (lane >> 5)))) & 0xFFu);
+    };
     auto compute = [&](int kstep, int set, int buf) {
-        const int w = (kstep % SKS) * 8;  // 16-byte chunk of the window inside the LDS chunk
+        const int w = (kstep % SKS_) * (SW / 8);  // 16-byte chunk of the step inside the LDS chunk
+        // MFMA q of the step takes chunk 8*(q>>1) + 2*(lane>>4) + (q&1) of the step's window
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int q = 0; q < SW / 32; ++q) {
+            const int h = q & 1;
             bf16x8 g, u;
             if constexpr (W8) {
-                g = decode8(rb[set][0][2 * h], rb[set][0][2 * h + 1], e8m0_factor(rs[set][0]));
-                u = decode8(rb[set][2][2 * h], rb[set][2][2 * h + 1], e8m0_factor(rs[set][1]));
+                const int l = q >> 1, j = kstep % SKS_;
+                g = decode8(rb[set][l][2 * h], rb[set][l][2 * h + 1], scale_of(0, j, l));
+                u = decode8(rb[set][2 + l][2 * h], rb[set][2 + l][2 * h + 1], scale_of(1, j, l));
             } else {
                 g = __builtin_bit_cast(bf16x8, rb[set][h]);
                 u = __builtin_bit_cast(bf16x8, rb[set][2 + h]);
@@ -284,7 +304,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
                 const bf16x8 a = *(const bf16x8*)(lds + buf * (ROWS * SKC) +
-                                                  s_off(r * 16 + (lane & 15), w + 2 * (lane >> 4) + h));
+                                                  s_off(r * 16 + (lane & 15), w + 8 * (q >> 1) + 2 * (lane >> 4) + h));
                 acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g, acc[r][0], 0, 0, 0);
                 acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u, acc[r][1], 0, 0, 0);
             }
@@ -296,6 +316,8 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     __builtin_amdgcn_sched_barrier(0);
     load_a(1);
     __builtin_amdgcn_sched_barrier(0);
+    load_s(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < RING - 1; ++s) {
         load_b(s, s);
@@ -304,9 +326,14 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     lds_barrier();
     for (int ck = 0; ck < nchunk; ++ck) {
         const int buf = ck & 1;
+        if constexpr (W8) {
+            sc[0] = scn[0];
+            sc[1] = scn[1];
+            load_s(ck + 1);
+        }
 #pragma unroll
-        for (int j = 0; j < SKS; ++j) {  // SKS is a multiple of RING: ring slots are static
-            const int kt = ck * SKS + j;
+        for (int j = 0; j < SKS_; ++j) {  // SKS_ is a multiple of RING: ring slots are static
+            const int kt = ck * SKS_ + j;
             __builtin_amdgcn_sched_barrier(0);
             load_b(kt + RING - 1, (j + RING - 1) % RING);
             compute(kt, j % RING, buf);

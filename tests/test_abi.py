@@ -128,6 +128,7 @@ def test_forward_fp8_validation_happens_before_launch():
         sc = [FAKE, FAKE, FAKE]
         sc[i] = None
         assert _raw_forward_fp8(s, need, scales=tuple(sc)) == bm.BEAM_ERR_INVALID_ARG
+    assert _raw_forward_fp8(s, need, scales=(FAKE, FAKE + 4, FAKE)) == bm.BEAM_ERR_INVALID_ARG   # misaligned
     assert _raw_forward_fp8(s, need, w=None) == bm.BEAM_ERR_INVALID_ARG
     assert _raw_forward_fp8(s, need, w=FAKE + 8) == bm.BEAM_ERR_INVALID_ARG   # codes are read 16 bytes at a time
     sf = _beam(T=64, H=256, I=128, dtype="f32")
