@@ -216,18 +216,18 @@ def summarize(cfg, r, steps, warmup):
     }
 
 
-def cpu_baseline(cfg, hw, n_tokens):
+def cpu_baseline(cfg, hw, n_tokens, w_scales=None):
     """The oracle, as it stands, on a seeded sample of the workload's tokens."""
     import oracle
     import synth
     from synth.configs import make_inputs
-    inp = make_inputs(cfg, weights=hw)
+    inp = make_inputs(cfg, weights=hw, w_scales=w_scales)
     tok = synth.subset(cfg.seed_base + 555, 98, cfg.T, n_tokens)
     t0 = time.perf_counter()
     x = inp.x[tok]
     u = oracle.rmsnorm_pinned(x, inp.pre_gain, cfg.eps) if cfg.sublayer else x
     r = oracle.route(u, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, want_margin=False)
-    y = oracle.experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w)
+    y = oracle.experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, w_scales=inp.w_scales)
     if cfg.sublayer:
         oracle.post_residual(y, x, inp.post_gain, cfg.eps, cfg.residual_k)
     dt = time.perf_counter() - t0
@@ -236,13 +236,13 @@ def cpu_baseline(cfg, hw, n_tokens):
                 n_tokens, cfg.name, " + norms" if cfg.sublayer else "", dt)}
 
 
-def sweep(base, hw, dw, sizes, steps, warmup, md_path=""):
+def sweep(base, hw, dw, sizes, steps, warmup, md_path="", scales=None):
     """The layer at several token counts with the decode workload's input distributions
     (serving shapes between decode and prefill); one JSON line per size."""
     rows = []
     for T in sizes:
         c = base.replace(name="serve_t%d" % T, T=T)
-        r = run_workload(c, hw, dw, steps, warmup)
+        r = run_workload(c, hw, dw, steps, warmup, scales=scales)
         s = summarize(c, r, steps, warmup)
         row = {"workload": c.name, "T": T, "tokens_per_s": s["tokens_per_s"], "ms_per_step": s["ms_per_step"],
                "gate_up_ms": s["stages_ms"]["gate_up"], "down_ms": s["stages_ms"]["down"],
@@ -278,7 +278,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_t8192",
-                    choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768"])
+                    choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768", "decode_t64_fp8",
+                             "prefill_t8192_fp8"])
     ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -321,16 +322,22 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+    scales = None
+    if cfg.weights == "fp8":   # the primary workload reads 8-bit weights: quantize, keep only those
+        from synth.configs import fp8_weights
+        hw, hs = fp8_weights(hw)
+        scales = (hs, tuple(dev(a) for a in hs))
     dw = tuple(dev(a) for a in hw)
     torch.cuda.synchronize()
     log("weights uploaded")
 
     if args.sweep:
-        sweep(CONFIGS["decode_t64"], hw, dw, [int(t) for t in args.sweep.split(",")], args.steps, args.warmup,
-              args.sweep_md)
+        base = CONFIGS["decode_t64_fp8" if cfg.weights == "fp8" else "decode_t64"]
+        sweep(base, hw, dw, [int(t) for t in args.sweep.split(",")], args.steps, args.warmup, args.sweep_md,
+              scales=scales)
         return
 
-    prim = run_workload(cfg, hw, dw, args.steps, args.warmup)
+    prim = run_workload(cfg, hw, dw, args.steps, args.warmup, scales=scales)
     s = summarize(cfg, prim, args.steps, args.warmup)
     log("primary %s: %.3f ms/step" % (cfg.name, s["ms_per_step"]))
     line = {
@@ -344,7 +351,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if cfg.weights != "fp8" else "bf16 activations, e4m3 weights",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "n_group": cfg.n_group,
                    "topk_group": cfg.topk_group, "top_k": cfg.top_k, "routed_scaling": cfg.rho,
@@ -357,7 +364,7 @@ def main():
         "max_expert_load": s["max_expert_load"],
         "empty_experts": s["empty_experts"],
     }
-    if args.secondary and args.secondary != "none" and args.secondary != cfg.name:
+    if args.secondary and args.secondary != "none" and args.secondary != cfg.name and cfg.weights != "fp8":
         c2 = CONFIGS[args.secondary]
         r2 = run_workload(c2, hw, dw, args.steps, args.warmup)
         s2 = summarize(c2, r2, args.steps, args.warmup)
@@ -388,7 +395,7 @@ def main():
         del dq, ds, hq, hs
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, hw, args.cpu_tokens)
+        line["cpu_baseline"] = cpu_baseline(cfg, hw, args.cpu_tokens, w_scales=scales[0] if scales else None)
     print(json.dumps(line), flush=True)
 
 
