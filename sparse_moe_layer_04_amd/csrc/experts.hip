@@ -224,8 +224,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     constexpr int AL = ACH / THREADS;            // per thread
     static_assert(AL * THREADS == ACH, "activation chunk split");
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
-    // a step is 64 k for bf16 weights (one 128-byte line per row) and 128 k for E4M3 (one
-    // 128-byte line per row: two 16-byte loads per lane, 64 bytes apart)
+    // a step is one 128-byte line of each weight row: 64 k of bf16 or 128 k of E4M3 codes
     constexpr int SW = W8 ? 128 : 64;
     constexpr int SKS_ = SKC / SW;               // steps per activation chunk
     static_assert(SKS_ % RING == 0, "ring slots are static inside a chunk");
@@ -251,60 +250,74 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
         for (int i = 0; i < AL; ++i) *(u32x4*)(lds + buf * (ROWS * SKC) + alds[i]) = sa[i];
     };
-    // weights: per 64 k, the lane's elements 16*(lane>>4) .. +15 of its two 16-row blocks
-    // (bf16: the 16-byte chunks 2*(lane>>4) and 2*(lane>>4)+1 of the row's 128-byte window;
-    // E4M3: one 16-byte load, and a second one for the step's other 64 k)
+    // weights: in each step lane (row, g = lane>>4) of a 16-row block loads the 32 bytes at
+    // 32*g of its row's 128-byte line (two 16-byte loads), so every load instruction covers
+    // whole lines: the elements 16*g .. +15 of the step (bf16) or 32*g .. +31 (E4M3, exactly
+    // one 32-element scale block)
     constexpr int BPE = W8 ? 1 : 2;
-    const uint8_t* b0 = c.bp0 + ((lane >> 4) * 16 - (lane >> 4) * 8) * BPE;
-    const uint8_t* b1 = c.bp1 + ((lane >> 4) * 16 - (lane >> 4) * 8) * BPE;
+    const uint8_t* b0 = c.bp0 + (lane >> 4) * (32 - 8 * BPE);
+    const uint8_t* b1 = c.bp1 + (lane >> 4) * (32 - 8 * BPE);
     u32x4 rb[RING][4];
     auto load_b = [&](int kstep, int set) {
-        const int k0 = (kstep < nk ? kstep : nk - 1) * SW;
+        const int k0 = (kstep < nk ? kstep : nk - 1) * SW * BPE;
+        rb[set][0] = *(const u32x4*)(b0 + k0);
+        rb[set][1] = *(const u32x4*)(b0 + k0 + 16);
+        rb[set][2] = *(const u32x4*)(b1 + k0);
+        rb[set][3] = *(const u32x4*)(b1 + k0 + 16);
+    };
+    // E4M3 scales.  A chunk of SKC = 512 k is 16 scale bytes per row: byte 4j + g scales
+    // the codes of lane group g in step j.  Lane (row, g) loads the 16 bytes of chunk 4m + g
+    // (64 bytes per row per load, one load per row block for four chunks, one group ahead);
+    // at each chunk every lane fetches the 4 dwords of its chunk from lane (row, chunk & 3)
+    // with ds_bpermute and keeps byte g of dword j for step j.
+    const int ngrp = (nchunk + 3) >> 2;
+    u32x4 sg[2] = {}, sgn[2] = {};
+    uint32_t sc[2][4] = {};
+    auto load_s = [&](int grp) {
         if constexpr (W8) {
-            rb[set][0] = *(const u32x4*)(b0 + k0);
-            rb[set][1] = *(const u32x4*)(b0 + k0 + 64);
-            rb[set][2] = *(const u32x4*)(b1 + k0);
-            rb[set][3] = *(const u32x4*)(b1 + k0 + 64);
-        } else {
-            rb[set][0] = *(const u32x4*)(b0 + 2 * k0);
-            rb[set][1] = *(const u32x4*)(b0 + 2 * k0 + 16);
-            rb[set][2] = *(const u32x4*)(b1 + 2 * k0);
-            rb[set][3] = *(const u32x4*)(b1 + 2 * k0 + 16);
+            const int m = grp < ngrp ? grp : ngrp - 1;
+            int off = 64 * m + 16 * (lane >> 4);
+            off = off < (c.K >> 5) - 16 ? off : (c.K >> 5) - 16;   // past the row's end: unused
+            sgn[0] = *(const u32x4*)(c.sp0 + off);
+            sgn[1] = *(const u32x4*)(c.sp1 + off);
         }
     };
-    // E4M3 scales: the 16 scale bytes of an activation chunk (4 steps x 4 blocks of 32 k) of
-    // each of the lane's two rows, one 16-byte load per row and chunk, one chunk ahead; byte
-    // 4j + 2l + (lane>>5) scales load l (0, 1) of step j of the chunk
-    u32x4 sc[2] = {}, scn[2] = {};
-    auto load_s = [&](int chunk) {
+    auto fetch_s = [&](int ck) {
         if constexpr (W8) {
-            const int ck = chunk < nchunk ? chunk : nchunk - 1;
-            scn[0] = *(const u32x4*)(c.sp0 + ck * 16);
-            scn[1] = *(const u32x4*)(c.sp1 + ck * 16);
+            const int src = ((lane & 15) + 16 * (ck & 3)) << 2;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sc[b][j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg[b][j]);
         }
     };
-    auto scale_of = [&](int blk, int j, int l) {
-        return e8m0_factor((sc[blk][j] >> (8 * (2 * l + (lane >> 5)))) & 0xFFu);
-    };
+    auto scale_of = [&](int blk, int j) { return e8m0_factor((sc[blk][j] >> (8 * (lane >> 4))) & 0xFFu); };
     auto compute = [&](int kstep, int set, int buf) {
         const int w = (kstep % SKS_) * (SW / 8);  // 16-byte chunk of the step inside the LDS chunk
-        // MFMA q of the step takes chunk 8*(q>>1) + 2*(lane>>4) + (q&1) of the step's window
+        constexpr int NQ = SW / 32;               // MFMAs per block and step
+        float s0 = 0.f, s1 = 0.f;
+        if constexpr (W8) {
+            s0 = scale_of(0, kstep % SKS_);
+            s1 = scale_of(1, kstep % SKS_);
+        }
+        // MFMA q of the step takes the lane's elements 8q .. 8q+7: chunk NQ*(lane>>4) + q
+        // of the step's window
 #pragma unroll
-        for (int q = 0; q < SW / 32; ++q) {
-            const int h = q & 1;
+        for (int q = 0; q < NQ; ++q) {
             bf16x8 g, u;
             if constexpr (W8) {
-                const int l = q >> 1, j = kstep % SKS_;
-                g = decode8(rb[set][l][2 * h], rb[set][l][2 * h + 1], scale_of(0, j, l));
-                u = decode8(rb[set][2 + l][2 * h], rb[set][2 + l][2 * h + 1], scale_of(1, j, l));
+                const int l = q >> 1, h = q & 1;
+                g = decode8(rb[set][l][2 * h], rb[set][l][2 * h + 1], s0);
+                u = decode8(rb[set][2 + l][2 * h], rb[set][2 + l][2 * h + 1], s1);
             } else {
-                g = __builtin_bit_cast(bf16x8, rb[set][h]);
-                u = __builtin_bit_cast(bf16x8, rb[set][2 + h]);
+                g = __builtin_bit_cast(bf16x8, rb[set][q]);
+                u = __builtin_bit_cast(bf16x8, rb[set][2 + q]);
             }
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
                 const bf16x8 a = *(const bf16x8*)(lds + buf * (ROWS * SKC) +
-                                                  s_off(r * 16 + (lane & 15), w + 8 * (q >> 1) + 2 * (lane >> 4) + h));
+                                                  s_off(r * 16 + (lane & 15), w + NQ * (lane >> 4) + q));
                 acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g, acc[r][0], 0, 0, 0);
                 acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u, acc[r][1], 0, 0, 0);
             }
@@ -327,9 +340,12 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     for (int ck = 0; ck < nchunk; ++ck) {
         const int buf = ck & 1;
         if constexpr (W8) {
-            sc[0] = scn[0];
-            sc[1] = scn[1];
-            load_s(ck + 1);
+            if ((ck & 3) == 0) {
+                sg[0] = sgn[0];
+                sg[1] = sgn[1];
+                load_s((ck >> 2) + 1);
+            }
+            fetch_s(ck);
         }
 #pragma unroll
         for (int j = 0; j < SKS_; ++j) {  // SKS_ is a multiple of RING: ring slots are static

@@ -139,6 +139,14 @@ MID_CASES = {
                                           seed_base=23000),
     "mid_fp8_sublayer_t333": mid_config("mid_fp8_sublayer_t333", 333, sublayer=True, residual_k=40,
                                         weights="fp8", seed_base=24000),
+    # K = 2560 and 1536 (5 and 3 activation chunks of 512): the decode kernel's streaming
+    # loop over several chunks, and with 8-bit weights its scale groups of four chunks
+    # (the second group partial)
+    "mid_decode_h2560_t12": mid_config("mid_decode_h2560_t12", 12, H=2560, I=1536, E=16, n_group=4, topk_group=2,
+                                       top_k=4, wr_std=math.sqrt(1.0 / 2560), seed_base=25000),
+    "mid_fp8_decode_h2560_t12": mid_config("mid_fp8_decode_h2560_t12", 12, H=2560, I=1536, E=16, n_group=4,
+                                           topk_group=2, top_k=4, weights="fp8", wr_std=math.sqrt(1.0 / 2560),
+                                           seed_base=26000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }
