@@ -55,6 +55,8 @@ def _load():
         lib.oracle_experts.restype = None
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_value.restype = f64
+        lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_value.restype = f64
         lib.oracle_post_residual.argtypes = [vp, vp, i32, vp, f32, i64, i64, f64, vp]
         lib.oracle_post_residual.restype = None
         lib.oracle_threads.argtypes = []
@@ -133,21 +135,34 @@ def e4m3_value(code: int) -> float:
     return float(_load().oracle_e4m3_value(int(code)))
 
 
+def e2m1_value(code: int) -> float:
+    """The value of one OCP FP4 E2M1 code, 0..15 (the oracle's decoding)."""
+    return float(_load().oracle_e2m1_value(int(code)))
+
+
 def experts(act: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, idx: np.ndarray,
             w: np.ndarray, tokens: Optional[np.ndarray] = None, w_scales=None) -> np.ndarray:
     """y[n] = sum_j w[t,j] * SwiGLU-expert_{idx[t,j]}(act[t]) for t = tokens[n]; fp64 [n,H].
 
     Weights are fp32, bf16 (uint16 bit patterns) or, with ``w_scales`` = (s_gate, s_up,
-    s_down), OCP FP8 E4M3 codes (uint8) with one E8M0 scale byte per 32 elements of a row."""
+    s_down), one E8M0 scale byte per 32 elements of a row and either OCP FP8 E4M3 codes
+    (uint8, the bf16 shapes) or OCP FP4 E2M1 codes two per byte (uint8, the last dimension
+    halved; the even element in the low nibble)."""
     act = _c(act)
     T, H = act.shape
     E, I, H2 = w_gate.shape
-    assert H2 == H and w_up.shape == (E, I, H) and w_down.shape == (E, H, I)
+    packed = w_scales is not None and 2 * H2 == H
+    if packed:
+        assert w_up.shape == (E, I, H // 2) and w_down.shape[:2] == (E, H)
+        I2 = w_down.shape[2]
+        assert 2 * I2 == I
+    else:
+        assert H2 == H and w_up.shape == (E, I, H) and w_down.shape == (E, H, I)
     if w_scales is not None:
         assert w_gate.dtype == w_up.dtype == w_down.dtype == np.uint8
         sg, su, sd = (np.ascontiguousarray(a, dtype=np.uint8) for a in w_scales)
         assert sg.shape == (E, I, H // 32) and su.shape == (E, I, H // 32) and sd.shape == (E, H, I // 32)
-        fmt, sp = 2, (sg.ctypes.data, su.ctypes.data, sd.ctypes.data)
+        fmt, sp = (3 if packed else 2), (sg.ctypes.data, su.ctypes.data, sd.ctypes.data)
     else:
         fmt = _is_bf16(w_gate)
         assert _is_bf16(w_up) == fmt and _is_bf16(w_down) == fmt

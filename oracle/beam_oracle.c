@@ -85,19 +85,37 @@ double oracle_e4m3_value(uint8_t code) {
     return sgn ? -v : v;
 }
 
+/* ---- 4-bit expert weights (MXFP4) ----------------------------------------------
+ * OCP FP4 E2M1: sign bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent field 0
+ * holds the subnormals 0 and 0.5; no infinities or NaN; largest 6.  Two codes per byte:
+ * the element with the even index in bits 0..3, the next one in bits 4..7.  The same E8M0
+ * scale byte per 32 consecutive elements of a row.
+ */
+double oracle_e2m1_value(uint8_t code) {
+    const int sgn = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    const double v = e == 0 ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
+    return sgn ? -v : v;
+}
+
 /* decoding tables for one call: value of every code and factor of every scale byte */
-typedef struct { double code[256], scale[256]; } fp8_tables;
+typedef struct { double code[256], fp4[16], scale[256]; } fp8_tables;
 
 static void fp8_tables_init(fp8_tables* t) {
     for (int i = 0; i < 256; ++i) {
         t->code[i] = oracle_e4m3_value((uint8_t)i);
         t->scale[i] = ldexp(1.0, i - 127);
     }
+    for (int i = 0; i < 16; ++i) t->fp4[i] = oracle_e2m1_value((uint8_t)i);
 }
 
-/* weight element i stored as fp32 (fmt 0), bf16 (fmt 1) or E4M3 with block scales sc (fmt 2) */
+/* weight element i stored as fp32 (fmt 0), bf16 (fmt 1), or with block scales sc as E4M3
+ * codes (fmt 2) or packed E2M1 codes (fmt 3) */
 static double wval(const void* p, const uint8_t* sc, int64_t i, int fmt, const fp8_tables* t) {
     if (fmt == 2) return t->code[((const uint8_t*)p)[i]] * t->scale[sc[i >> 5]];
+    if (fmt == 3) {
+        const uint8_t b = ((const uint8_t*)p)[i >> 1];
+        return t->fp4[(i & 1) ? b >> 4 : b & 15] * t->scale[sc[i >> 5]];
+    }
     return elem(p, i, fmt);
 }
 
@@ -268,8 +286,9 @@ int oracle_route(const void* act, int act_bf16, int64_t T, int64_t H, const floa
 /*
  * For each listed token tok[n] (n < n_tok): y[n, :] = sum_j wts[t,j] * FFN_{idx[t,j]}(act[t, :]),
  * j ascending, where FFN_e(u) = W_d[e] (silu(W_g[e] u) * (W_u[e] u)).
- * act [T,H]; w_gate, w_up [E,I,H]; w_down [E,H,I], all stored as w_fmt: fp32 (0), bf16 (1)
- * or E4M3 codes (2) with E8M0 block scales s_gate, s_up [E,I,H/32] and s_down [E,H,I/32];
+ * act [T,H]; w_gate, w_up [E,I,H]; w_down [E,H,I], all stored as w_fmt: fp32 (0), bf16 (1),
+ * E4M3 codes (2) or E2M1 codes two per byte (3), the last two with E8M0 block scales
+ * s_gate, s_up [E,I,H/32] and s_down [E,H,I/32];
  * idx [T,K]; wts [T,K] fp64.  y [n_tok,H] fp64.
  */
 void oracle_experts(const void* act, int act_bf16, int64_t H, int64_t I, const void* w_gate, const void* w_up,

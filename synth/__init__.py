@@ -44,6 +44,8 @@ def _load():
         lib.synth_words.restype = None
         lib.synth_quant_e4m3.argtypes = [vp, u64, u64, vp, vp]
         lib.synth_quant_e4m3.restype = None
+        lib.synth_quant_e2m1.argtypes = [vp, u64, u64, vp, vp]
+        lib.synth_quant_e2m1.restype = None
         _lib = lib
     return _lib
 
@@ -100,6 +102,21 @@ def quantize_e4m3(w: np.ndarray):
     codes = np.empty(w.shape, dtype=np.uint8)
     scales = np.empty(w.shape[:-1] + (cols // 32,), dtype=np.uint8)
     _load().synth_quant_e4m3(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def quantize_e2m1(w: np.ndarray):
+    """bf16 weights [..., K] (uint16 bit patterns, K % 32 == 0) in 4-bit storage (MXFP4): OCP
+    FP4 E2M1 codes two per byte [..., K/2] (the even element in the low nibble) and E8M0
+    block scales [..., K/32] (uint8), as described in synth.c."""
+    if w.dtype != np.uint16 or w.shape[-1] % 32:
+        raise ValueError("expected bf16 bit patterns with a last dimension divisible by 32")
+    w = np.ascontiguousarray(w)
+    cols = w.shape[-1]
+    rows = w.size // cols
+    codes = np.empty(w.shape[:-1] + (cols // 2,), dtype=np.uint8)
+    scales = np.empty(w.shape[:-1] + (cols // 32,), dtype=np.uint8)
+    _load().synth_quant_e2m1(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data)
     return codes, scales
 
 

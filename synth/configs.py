@@ -55,8 +55,9 @@ class Config:
     gain_std: float = 0.02
     seed_base: int = 0           # x-seed = seed_base + j
     weight_seed: Optional[int] = None  # None: same seed as x (config 0)
-    weights: str = "bf16"        # expert weight storage: "bf16", or "fp8" (E4M3 codes + E8M0 block
-                                 # scales from the bf16 draw, see synth.quantize_e4m3)
+    weights: str = "bf16"        # expert weight storage: "bf16", "fp8" (E4M3 codes + E8M0 block
+                                 # scales from the bf16 draw, see synth.quantize_e4m3) or "mxfp4"
+                                 # (E2M1 codes two per byte + E8M0 block scales, synth.quantize_e2m1)
 
     @property
     def P(self) -> int:
@@ -85,9 +86,14 @@ CONFIGS = {
     # 32 elements, quantized from the same bf16 draw)
     "decode_t64_fp8": Config("decode_t64_fp8", T=64, bias="uniform:0.05", seed_base=1000, weights="fp8", **_BEAM),
     "prefill_t8192_fp8": Config("prefill_t8192_fp8", T=8192, bias="zero", seed_base=2000, weights="fp8", **_BEAM),
+    # ... and with 4-bit expert weights (MXFP4: E2M1 codes + E8M0 scales per 32 elements)
+    "decode_t64_mxfp4": Config("decode_t64_mxfp4", T=64, bias="uniform:0.05", seed_base=1000, weights="mxfp4",
+                               **_BEAM),
+    "prefill_t8192_mxfp4": Config("prefill_t8192_mxfp4", T=8192, bias="zero", seed_base=2000, weights="mxfp4",
+                                  **_BEAM),
 }
 CONFIG_ORDER = ["tiny_f32", "decode_t64", "prefill_t8192", "skew_t6000", "sublayer_t32768", "serve_t256",
-                "serve_t1024", "decode_t64_fp8", "prefill_t8192_fp8"]
+                "serve_t1024", "decode_t64_fp8", "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4"]
 
 
 def seed_index(name: str) -> int:
@@ -111,7 +117,7 @@ class MoEInputs:
     w_down: np.ndarray       # [E,H,I]
     pre_gain: Optional[np.ndarray] = None   # [H] float32
     post_gain: Optional[np.ndarray] = None  # [H] float32
-    w_scales: Optional[tuple] = None        # fp8 weights: E8M0 scales of (w_gate, w_up, w_down)
+    w_scales: Optional[tuple] = None        # fp8 / mxfp4 weights: E8M0 scales of (w_gate, w_up, w_down)
 
 
 def _act(cfg: Config, seed: int, tid: int, shape, std: float, mean: float = 0.0):
@@ -128,6 +134,24 @@ def fp8_weights(weights):
     wr, wg, wu, wd = weights
     (cg, sg), (cu, su), (cd, sd) = quantize_e4m3(wg), quantize_e4m3(wu), quantize_e4m3(wd)
     return (wr, cg, cu, cd), (sg, su, sd)
+
+
+def mxfp4_weights(weights):
+    """(w_router, w_gate, w_up, w_down) with bf16 experts -> the same tuple with packed E2M1
+    expert codes (last dimension halved), and the (s_gate, s_up, s_down) E8M0 block scales."""
+    from . import quantize_e2m1
+    wr, wg, wu, wd = weights
+    (cg, sg), (cu, su), (cd, sd) = quantize_e2m1(wg), quantize_e2m1(wu), quantize_e2m1(wd)
+    return (wr, cg, cu, cd), (sg, su, sd)
+
+
+def quantized_weights(cfg: Config, weights):
+    """The expert weights of a config in its storage format: (weights, scales or None)."""
+    if cfg.weights == "fp8":
+        return fp8_weights(weights)
+    if cfg.weights == "mxfp4":
+        return mxfp4_weights(weights)
+    return weights, None
 
 
 def expert_weights(cfg: Config, seed: Optional[int] = None):
@@ -161,15 +185,15 @@ def make_bias(cfg: Config, seed: int) -> np.ndarray:
 
 def make_inputs(cfg: Config, j: Optional[int] = None, weights=None, w_scales=None) -> MoEInputs:
     """All inputs of a config.  ``weights`` may pass a pre-generated (wr, wg, wu, wd) tuple
-    (for an fp8 config: the E4M3 codes, with their ``w_scales``)."""
+    (for an fp8 or mxfp4 config: the codes, with their ``w_scales``)."""
     from . import normal_f32
     if j is None:
         j = seed_index(cfg.name)
     xs = cfg.seed_base + j
     if weights is None:
         weights = expert_weights(cfg, seed=(xs if cfg.weight_seed is None else cfg.weight_seed))
-        if cfg.weights == "fp8":
-            weights, w_scales = fp8_weights(weights)
+        if cfg.weights != "bf16":
+            weights, w_scales = quantized_weights(cfg, weights)
     wr, wg, wu, wd = weights
     x = _act(cfg, xs, TID_X, (cfg.T, cfg.H), cfg.x_std)
     bias = make_bias(cfg, xs)

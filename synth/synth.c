@@ -143,3 +143,52 @@ void synth_quant_e4m3(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t* 
         for (int i = 0; i < 32; ++i) codes[(uint64_t)b * 32 + i] = e4m3_nearest(bf16_bits_to_double(src[i]) * inv);
     }
 }
+
+/*
+ * Weights stored in 4 bits (MXFP4; an input format, no layer arithmetic).  OCP FP4 E2M1
+ * codes (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6; no infinities or NaN), two per byte with the even element in bits 0..3, and one
+ * E8M0 scale byte s per 32 consecutive elements of a row.  Per block: s = 127 +
+ * ceil(log2(amax / 6)) (127 for an all-zero block), clamped to [1, 254]; each element w
+ * becomes the E2M1 value nearest to w / 2^(s - 127), ties to the even code.
+ */
+static uint8_t e2m1_nearest(double x) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const uint8_t sign = x < 0 ? 8 : 0;
+    const double a = fabs(x);
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        const double d = fabs(a - mag[c]), db = fabs(a - mag[best]);
+        if (d < db || (d == db && (c & 1) == 0)) best = c;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* w [rows, cols] bf16 bit patterns (cols % 32 == 0) -> codes [rows, cols/2], scales [rows, cols/32] */
+void synth_quant_e2m1(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t* codes, uint8_t* scales) {
+    const int64_t nblk = (int64_t)(rows * (cols / 32));
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; ++b) {
+        const uint16_t* src = w + (uint64_t)b * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            const double v = fabs(bf16_bits_to_double(src[i]));
+            if (v > amax) amax = v;
+        }
+        int s = 127;
+        if (amax > 0.0) {
+            int e;
+            const double f = frexp(amax / 6.0, &e);
+            s = 127 + (f == 0.5 ? e - 1 : e);
+            if (s < 1) s = 1;
+            if (s > 254) s = 254;
+        }
+        scales[b] = (uint8_t)s;
+        const double inv = ldexp(1.0, 127 - s);
+        for (int i = 0; i < 32; i += 2) {
+            const uint8_t lo = e2m1_nearest(bf16_bits_to_double(src[i]) * inv);
+            const uint8_t hi = e2m1_nearest(bf16_bits_to_double(src[i + 1]) * inv);
+            codes[(uint64_t)b * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}

@@ -33,7 +33,14 @@ MUTANTS = {
     "e4m3_subnormal_as_normal": ("e == 0 ? ldexp((double)m, -9)", "e == 0 ? ldexp(1.0 + m / 8.0, -7)"),
     "e4m3_mantissa_4_bits": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 16.0, e - 7)"),
     "e8m0_scale_bias": ("t->scale[i] = ldexp(1.0, i - 127);", "t->scale[i] = ldexp(1.0, i - 128);"),
-    "scale_block_of_16": ("t->scale[sc[i >> 5]]", "t->scale[sc[i >> 4]]"),
+    "scale_block_of_16": ("t->code[((const uint8_t*)p)[i]] * t->scale[sc[i >> 5]]",
+                          "t->code[((const uint8_t*)p)[i]] * t->scale[sc[i >> 4]]"),
+    "e2m1_exponent_bias_2": ("ldexp(1.0 + m / 2.0, e - 1)", "ldexp(1.0 + m / 2.0, e - 2)"),
+    "e2m1_subnormal_as_normal": ("e == 0 ? 0.5 * m", "e == 0 ? ldexp(1.0 + m / 2.0, -1)"),
+    "e2m1_sign_bit_2": ("const int sgn = (code >> 3) & 1", "const int sgn = (code >> 2) & 1"),
+    "e2m1_nibbles_swapped": ("(i & 1) ? b >> 4 : b & 15", "(i & 1) ? b & 15 : b >> 4"),
+    "e2m1_scale_block_of_16": ("t->fp4[(i & 1) ? b >> 4 : b & 15] * t->scale[sc[i >> 5]]",
+                               "t->fp4[(i & 1) ? b >> 4 : b & 15] * t->scale[sc[i >> 4]]"),
     "weights_reversed": ("double wj = wts[t * K + j];", "double wj = wts[t * K + (K - 1 - j)];"),
     "rms_sum_not_mean": ("float r = (float)(1.0 / sqrt(ss / (double)H + (double)eps));",
                          "float r = (float)(1.0 / sqrt(ss + (double)eps));"),

@@ -477,6 +477,76 @@ def test_fp8_layer_equals_the_layer_on_the_decoded_weights():
     assert not np.allclose(y_bad, y_fp8)
 
 
+def test_e2m1_values_fixed_by_the_format():
+    # OCP microscaling specification, FP4 E2M1: bias 1, magnitudes 0, 0.5 (the one
+    # subnormal), 1, 1.5, 2, 3, 4, 6 (the largest); bit 3 is the sign; no infinities or NaN
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert oracle.e2m1_value(c) == mags[c]
+        assert oracle.e2m1_value(8 | c) == -mags[c]
+    assert math.copysign(1.0, oracle.e2m1_value(8)) < 0
+
+
+def _representable_blocks_e2m1(rows, cols, seed):
+    """bf16 weights whose every 32-element block is exactly E2M1 values times 2^(s-127),
+    with one element at 6 * 2^(s-127), so the block scale is s; returns (bf16, packed, s)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+    codes[codes == 8] = 0                                       # the quantizer writes +0 for zero
+    codes[:, ::32] = 7 | (codes[:, ::32] & 8)                   # the block maximum
+    s = rng.integers(100, 130, size=(rows, cols // 32), dtype=np.uint8)
+    vals = np.array([oracle.e2m1_value(c) for c in range(16)])
+    w = vals[codes] * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)   # even element in the low nibble
+    return synth.f32_to_bf16(w.astype(np.float32)), packed, s
+
+
+def test_e2m1_quantizer_round_trips_representable_blocks():
+    w, packed, s = _representable_blocks_e2m1(6, 128, 41)
+    c2, s2 = synth.quantize_e2m1(w)
+    assert c2.shape == (6, 64) and (c2 == packed).all() and (s2 == s).all()
+
+
+def test_mxfp4_layer_equals_the_layer_on_the_decoded_weights():
+    H, I, E, T = 64, 32, 4, 5
+    wg, cg, sg = _representable_blocks_e2m1(E * I, H, 51)
+    wu, cu, su = _representable_blocks_e2m1(E * I, H, 52)
+    wd, cd, sd = _representable_blocks_e2m1(E * H, I, 53)
+    rng = np.random.default_rng(9)
+    u = synth.f32_to_bf16(rng.normal(size=(T, H)).astype(np.float32))
+    idx = rng.integers(0, E, size=(T, 2)).astype(np.int32)
+    wts = rng.uniform(0.1, 1.0, size=(T, 2))
+    scales = (sg.reshape(E, I, H // 32), su.reshape(E, I, H // 32), sd.reshape(E, H, I // 32))
+    y_bf16 = oracle.experts(u, wg.reshape(E, I, H), wu.reshape(E, I, H), wd.reshape(E, H, I), idx, wts)
+    y_fp4 = oracle.experts(u, cg.reshape(E, I, H // 2), cu.reshape(E, I, H // 2), cd.reshape(E, H, I // 2), idx,
+                           wts, w_scales=scales)
+    assert (y_bf16 == y_fp4).all()
+    # the nibble order is seen: codes with their two nibbles swapped give another layer
+    sw = lambda c: ((c >> 4) | (c << 4)).astype(np.uint8)
+    y_bad = oracle.experts(u, sw(cg).reshape(E, I, H // 2), sw(cu).reshape(E, I, H // 2),
+                           sw(cd).reshape(E, H, I // 2), idx, wts, w_scales=scales)
+    assert not np.allclose(y_bad, y_fp4)
+
+
+def test_e2m1_quantizer_error_bound_on_gaussian_weights():
+    # nearest-value rounding: |w - q| <= half the E2M1 spacing around w/2^(s-127) times the
+    # scale (spacing 0.5 below 2, 1 in [2, 4), 2 in [4, 6]); |w| <= 6 * 2^(s-127)
+    w = synth.normal_bf16(7, 4, (16, 256), 0.0, 0.02)
+    packed, s = synth.quantize_e2m1(w)
+    codes = np.empty((16, 256), dtype=np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = packed & 15, packed >> 4
+    vals = np.array([oracle.e2m1_value(c) for c in range(16)])
+    scale = np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    q = vals[codes] * scale
+    wf = synth.bf16_to_f32(w).astype(np.float64)
+    x = np.abs(wf) / scale
+    assert (x <= 6.0).all()
+    spacing = np.where(x < 2.0, 0.5, np.where(x < 4.0, 1.0, 2.0)) * scale
+    assert (np.abs(wf - q) <= 0.5 * spacing * (1 + 1e-12)).all()
+    # the block maximum lands in the top binade [3, 6] (the scale is the smallest that fits)
+    assert (x.reshape(16, 8, 32).max(axis=2) > 3.0).all()
+
+
 def test_quantizer_error_bound_on_gaussian_weights():
     # nearest-value rounding: |w - q| <= half the E4M3 spacing at q's binade times the scale
     w = synth.normal_bf16(7, 3, (16, 256), 0.0, 0.02)
