@@ -40,8 +40,9 @@ def kernel_source_hash() -> str:
 
 
 def weight_bytes_per_element(cfg):
-    """bf16: 2; 8-bit storage: 1 byte per code plus one scale byte per 32 elements."""
-    return 1.0 + 1.0 / 32 if cfg.weights == "fp8" else 2.0
+    """bf16: 2; 8-bit storage: 1 byte per code plus one scale byte per 32 elements; MXFP4:
+    half a byte per code plus the scale byte per 32."""
+    return {"fp8": 1.0 + 1.0 / 32, "mxfp4": 0.5 + 1.0 / 32}.get(cfg.weights, 2.0)
 
 
 def gate_up_work(cfg, n_touched):
@@ -167,7 +168,8 @@ def run_workload(cfg, hw, dw, steps, warmup, scales=None):
 
     def step(timer=None):
         bm.forward(shape, x, dw[0], bias, dw[1], dw[2], dw[3], out, ws, sublayer=sub, topk_idx=idx,
-                   stage_events=timer.events if timer else None, w_scales=scales[1] if scales else None)
+                   stage_events=timer.events if timer else None, w_scales=scales[1] if scales else None,
+                   w_format=cfg.code_format or "e4m3")
 
     for _ in range(warmup):
         step()
@@ -279,11 +281,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_t8192",
                     choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768", "decode_t64_fp8",
-                             "prefill_t8192_fp8"])
+                             "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4"])
     ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit-weight decode and prefill layers")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the decode and prefill layers with 8-bit and 4-bit expert weights")
     ap.add_argument("--sweep", default="", metavar="T1,T2,...",
                     help="time the layer on the decode workload's inputs at each token count (serving shapes) "
                          "and print one JSON line per size instead of the benchmark line")
@@ -323,16 +326,16 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     scales = None
-    if cfg.weights == "fp8":   # the primary workload reads 8-bit weights: quantize, keep only those
-        from synth.configs import fp8_weights
-        hw, hs = fp8_weights(hw)
+    if cfg.weights != "bf16":   # the primary workload reads quantized weights: quantize, keep only those
+        from synth.configs import quantized_weights
+        hw, hs = quantized_weights(cfg, hw)
         scales = (hs, tuple(dev(a) for a in hs))
     dw = tuple(dev(a) for a in hw)
     torch.cuda.synchronize()
     log("weights uploaded")
 
     if args.sweep:
-        base = CONFIGS["decode_t64_fp8" if cfg.weights == "fp8" else "decode_t64"]
+        base = CONFIGS["decode_t64" if cfg.weights == "bf16" else "decode_t64_" + cfg.weights]
         sweep(base, hw, dw, [int(t) for t in args.sweep.split(",")], args.steps, args.warmup, args.sweep_md,
               scales=scales)
         return
@@ -351,7 +354,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.weights != "fp8" else "bf16 activations, e4m3 weights",
+        "dtype": {"fp8": "bf16 activations, e4m3 weights", "mxfp4": "bf16 activations, e2m1 (mxfp4) weights"}.get(
+            cfg.weights, "bf16"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "n_group": cfg.n_group,
                    "topk_group": cfg.topk_group, "top_k": cfg.top_k, "routed_scaling": cfg.rho,
@@ -364,7 +368,7 @@ def main():
         "max_expert_load": s["max_expert_load"],
         "empty_experts": s["empty_experts"],
     }
-    if args.secondary and args.secondary != "none" and args.secondary != cfg.name and cfg.weights != "fp8":
+    if args.secondary and args.secondary != "none" and args.secondary != cfg.name and cfg.weights == "bf16":
         c2 = CONFIGS[args.secondary]
         r2 = run_workload(c2, hw, dw, args.steps, args.warmup)
         s2 = summarize(c2, r2, args.steps, args.warmup)
@@ -377,23 +381,26 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_fp8 and args.workload == "prefill_t8192":
         # the same layers with the expert weights in 8-bit storage (E4M3 codes + E8M0 scales
-        # per 32 elements; beam_moe_forward_fp8), quantized from the same bf16 weights
-        from synth.configs import fp8_weights
-        hq, hs = fp8_weights(hw)
-        dq, ds = tuple(dev(a) for a in hq), tuple(dev(a) for a in hs)
-        torch.cuda.synchronize()
-        line["fp8_weights"] = {}
-        for name in ("decode_t64_fp8", "prefill_t8192_fp8"):
-            c8 = CONFIGS[name]
-            r8 = run_workload(c8, hq, dq, args.steps, args.warmup, scales=(hs, ds))
-            s8 = summarize(c8, r8, args.steps, args.warmup)
-            log("fp8 %s: %.3f ms/step" % (name, s8["ms_per_step"]))
-            line["fp8_weights"][name] = {"tokens_per_s": s8["tokens_per_s"], "ms_per_step": s8["ms_per_step"],
-                                         "layer": s8["layer"], "stages_ms": s8["stages_ms"],
-                                         "gate_up": s8["gate_up"], "down": s8["down"],
-                                         "experts_touched": s8["experts_touched"]}
-        del dq, ds, hq, hs
-        torch.cuda.empty_cache()
+        # per 32 elements; beam_moe_forward_fp8) and in 4-bit storage (MXFP4: E2M1 codes +
+        # E8M0 scales; beam_moe_forward_mxfp4), quantized from the same bf16 weights
+        from synth.configs import quantized_weights
+        for fmt, key in (("fp8", "fp8_weights"), ("mxfp4", "mxfp4_weights")):
+            names = ("decode_t64_" + fmt, "prefill_t8192_" + fmt)
+            hq, hs = quantized_weights(CONFIGS[names[0]], hw)
+            dq, ds = tuple(dev(a) for a in hq), tuple(dev(a) for a in hs)
+            torch.cuda.synchronize()
+            line[key] = {}
+            for name in names:
+                c8 = CONFIGS[name]
+                r8 = run_workload(c8, hq, dq, args.steps, args.warmup, scales=(hs, ds))
+                s8 = summarize(c8, r8, args.steps, args.warmup)
+                log("%s %s: %.3f ms/step" % (fmt, name, s8["ms_per_step"]))
+                line[key][name] = {"tokens_per_s": s8["tokens_per_s"], "ms_per_step": s8["ms_per_step"],
+                                   "layer": s8["layer"], "stages_ms": s8["stages_ms"],
+                                   "gate_up": s8["gate_up"], "down": s8["down"],
+                                   "experts_touched": s8["experts_touched"]}
+            del dq, ds, hq, hs
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, hw, args.cpu_tokens, w_scales=scales[0] if scales else None)
     print(json.dumps(line), flush=True)

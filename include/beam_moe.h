@@ -207,6 +207,31 @@ beam_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, con
                                  const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w, void* moe_y,
                                  void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 
+/*
+ * beam_moe_forward with 4-bit expert weights (MXFP4; bf16 activations; shape->dtype must
+ * be BEAM_BF16, else BEAM_ERR_UNSUPPORTED).  Each weight is stored as an OCP FP4 E2M1 code
+ * (sign bit 3, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6; no infinities or NaN), two codes per byte: element 2i in bits 0..3 and element
+ * 2i+1 in bits 4..7.  Every 32 consecutive elements of a row along the reduction dimension
+ * share one E8M0 scale byte s, meaning 2^(s - 127); the weight is e2m1(code) * 2^(s - 127).
+ *   w_gate, w_up [E,I,H/2] and w_down [E,H,I/2]: packed E2M1 codes, the rows of the bf16
+ *            weights of beam_moe_forward at half a byte per element (16-byte aligned)
+ *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes (16-byte aligned),
+ *            s in 1..254, chosen so that every decoded weight is a normal bf16 number (or zero)
+ * Every other argument, the workspace and the results are as for beam_moe_forward.  The
+ * weights are decoded to bf16 exactly and the layer then computes exactly what
+ * beam_moe_forward computes on the decoded weights; the weight bytes read from memory are
+ * a quarter (plus 1/32 byte of scale per weight).  The pages quote a ~4.5-bit checkpoint
+ * format for another GPU family without its layout; this is the OCP microscaling MXFP4
+ * format, the 4-bit format of this GPU's matrix cores.
+ */
+beam_status beam_moe_forward_mxfp4(const beam_moe_shape* shape, const void* x, const float* w_router,
+                                   const float* bias, const uint8_t* w_gate, const uint8_t* w_up,
+                                   const uint8_t* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                   const uint8_t* s_down, const beam_sublayer* sub, void* out, int32_t* topk_idx,
+                                   float* topk_w, void* moe_y, void* ws, size_t ws_bytes, void* const* stage_events,
+                                   void* stream);
+
 /* Static description of a status code. */
 const char* beam_status_string(beam_status status);
 

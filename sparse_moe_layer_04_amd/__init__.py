@@ -34,7 +34,7 @@ STAGE_NAMES = ("prenorm", "router_logits", "router_select", "permute", "gate_up"
 
 # exported C symbols (declared in include/beam_moe.h)
 EXPORTS = ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward",
-           "beam_moe_forward_fp8", "beam_status_string", "beam_moe_abi_version")
+           "beam_moe_forward_fp8", "beam_moe_forward_mxfp4", "beam_status_string", "beam_moe_abi_version")
 
 
 class Shape(ctypes.Structure):
@@ -57,8 +57,9 @@ _lib.beam_moe_forward.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp
                                   _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
 _lib.beam_moe_forward_fp8.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.POINTER(Sublayer), _vp, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
+_lib.beam_moe_forward_mxfp4.argtypes = _lib.beam_moe_forward_fp8.argtypes
 for _f in ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward",
-           "beam_moe_forward_fp8"):
+           "beam_moe_forward_fp8", "beam_moe_forward_mxfp4"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.beam_status_string.argtypes = [ctypes.c_int]
 _lib.beam_status_string.restype = ctypes.c_char_p
@@ -142,9 +143,10 @@ def permute(shape: Shape, topk_idx, offsets, sorted_pairs, pair_pos, ws, stream=
 
 def forward(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, out, ws, sublayer: Optional[Sublayer] = None,
             topk_idx=None, topk_w=None, moe_y=None, stage_events: Optional[Sequence[int]] = None, stream=None,
-            w_scales=None):
-    """beam_moe_forward; with ``w_scales`` = (s_gate, s_up, s_down) the expert weights are E4M3
-    codes (uint8) with E8M0 block scales and beam_moe_forward_fp8 is called."""
+            w_scales=None, w_format: str = "e4m3"):
+    """beam_moe_forward; with ``w_scales`` = (s_gate, s_up, s_down) the expert weights are codes
+    with E8M0 block scales: E4M3 bytes (``w_format`` "e4m3", beam_moe_forward_fp8) or E2M1
+    codes two per byte ("e2m1", beam_moe_forward_mxfp4)."""
     ev = None
     if stage_events is not None:
         if len(stage_events) != NUM_STAGES + 1:
@@ -157,10 +159,13 @@ def forward(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, out, ws, subl
                                      _ptr(moe_y), _ptr(ws), _nbytes(ws), ev, _stream(stream)), "beam_moe_forward")
     else:
         sg, su, sd = w_scales
-        _check(_lib.beam_moe_forward_fp8(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
-                                         _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd), sub, _ptr(out),
-                                         _ptr(topk_idx), _ptr(topk_w), _ptr(moe_y), _ptr(ws), _nbytes(ws), ev,
-                                         _stream(stream)), "beam_moe_forward_fp8")
+        name = {"e4m3": "beam_moe_forward_fp8", "e2m1": "beam_moe_forward_mxfp4"}.get(w_format)
+        if name is None:
+            raise ValueError("w_format must be 'e4m3' or 'e2m1'")
+        _check(getattr(_lib, name)(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+                                   _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd), sub, _ptr(out),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(moe_y), _ptr(ws), _nbytes(ws), ev,
+                                   _stream(stream)), name)
 
 
 def sublayer(pre_gain, post_gain, eps: float, residual_k: float) -> Sublayer:

@@ -167,11 +167,13 @@ beam_status beam_moe_permute(const beam_moe_shape* shape, const int32_t* topk_id
 
 namespace {
 
-// E8M0 block scales of E4M3 expert weights (all three, or none for bf16/fp32 weights)
+// E8M0 block scales of quantized expert weights (all three, or none for bf16/fp32 weights)
+// and the storage format of the codes (beam::WF_E4M3 or beam::WF_E2M1)
 struct WeightScales {
     const uint8_t* gate;
     const uint8_t* up;
     const uint8_t* down;
+    int format;
 };
 
 beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float* w_router, const float* bias,
@@ -236,8 +238,9 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     void* h = at<void>(ws, L.h);
     void* ypair = at<void>(ws, L.ypair);
     if (bf16) {
-        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, sc ? sc->gate : nullptr, sc ? sc->up : nullptr, T, H,
-                                      I, E, K, sorted, tiles, ntiles, L.max_tiles, L.tile_rows, h, s));
+        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, sc ? sc->format : beam::WF_BF16,
+                                      sc ? sc->gate : nullptr, sc ? sc->up : nullptr, T, H, I, E, K, sorted, tiles,
+                                      ntiles, L.max_tiles, L.tile_rows, h, s));
     } else {
         BEAM_TRY(beam::launch_gate_up_f32(static_cast<const float*>(act), static_cast<const float*>(w_gate),
                                           static_cast<const float*>(w_up), H, I, K, sorted, idx, P,
@@ -245,8 +248,8 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     }
     BEAM_TRY(mark(BEAM_STAGE_DOWN));
     if (bf16) {
-        BEAM_TRY(beam::launch_down(h, true, w_down, sc ? sc->down : nullptr, P, H, I, E, sorted, tiles, ntiles,
-                                   L.max_tiles, L.tile_rows, ypair, s));
+        BEAM_TRY(beam::launch_down(h, true, w_down, sc ? sc->format : beam::WF_BF16, sc ? sc->down : nullptr, P, H,
+                                   I, E, sorted, tiles, ntiles, L.max_tiles, L.tile_rows, ypair, s));
     } else {
         BEAM_TRY(beam::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w_down), H, I, sorted,
                                        idx, P, static_cast<float*>(ypair), s));
@@ -276,7 +279,18 @@ beam_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, con
                                  const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down,
                                  const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w, void* moe_y,
                                  void* ws, size_t ws_bytes, void* const* stage_events, void* stream) {
-    const WeightScales sc{s_gate, s_up, s_down};
+    const WeightScales sc{s_gate, s_up, s_down, beam::WF_E4M3};
+    return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, &sc, sub, out, topk_idx, topk_w, moe_y, ws,
+                        ws_bytes, stage_events, stream);
+}
+
+beam_status beam_moe_forward_mxfp4(const beam_moe_shape* shape, const void* x, const float* w_router,
+                                   const float* bias, const uint8_t* w_gate, const uint8_t* w_up,
+                                   const uint8_t* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                   const uint8_t* s_down, const beam_sublayer* sub, void* out, int32_t* topk_idx,
+                                   float* topk_w, void* moe_y, void* ws, size_t ws_bytes, void* const* stage_events,
+                                   void* stream) {
+    const WeightScales sc{s_gate, s_up, s_down, beam::WF_E2M1};
     return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, &sc, sub, out, topk_idx, topk_w, moe_y, ws,
                         ws_bytes, stage_events, stream);
 }

@@ -90,17 +90,23 @@ inline int64_t max_tiles(int64_t P, int E, int tile_rows) { return (P + tile_row
 // rows per GEMM tile the forward pass uses for a given average load
 int gemm_tile_rows(int64_t P, int E, bool bf16);
 
+// expert weight storage: bf16, OCP FP8 E4M3 codes, or OCP FP4 E2M1 codes two per byte (the
+// last two with one E8M0 scale byte per 32 elements of a row along K)
+constexpr int WF_BF16 = 0, WF_E4M3 = 1, WF_E2M1 = 2;
+// bits per stored weight
+__host__ __device__ constexpr int wbits(int wf) { return wf == WF_BF16 ? 16 : wf == WF_E4M3 ? 8 : 4; }
+
 // h[row, :] = silu(A W_g^T) * (A W_u^T) for the expert-sorted rows (A = gathered token rows)
-// (act: T token rows; the activation and h tensors must stay below 4 GiB).  With s_gate and
-// s_up the weights are E4M3 codes with E8M0 scales per 32 elements of a row (else bf16).
-hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, const uint8_t* s_gate,
-                          const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
+// (act: T token rows; the activation and h tensors must stay below 4 GiB).  Weights stored
+// as `wf`; quantized formats come with s_gate and s_up (bf16: null).
+hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int wf,
+                          const uint8_t* s_gate, const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
                           const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                           int64_t max_tile_count, int tile_rows, void* h, hipStream_t s);
 
-// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T   (h: P rows; E4M3 weights with s_down)
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, const uint8_t* s_down, int64_t P, int H, int I,
-                       int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T   (h: P rows; quantized weights with s_down)
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t P, int H,
+                       int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s);
 
 // fp32 path (no tiles): one thread per output element

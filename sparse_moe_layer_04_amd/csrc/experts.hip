@@ -49,10 +49,11 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// ---- 8-bit weights: OCP FP8 E4M3 codes with one E8M0 scale byte per 32 elements of a
-// row along K (the weight is e4m3(code) * 2^(scale - 127)).  An E4M3 value times a power of
-// two is exactly a bf16 value (3 mantissa bits, exponents in range), so the weights are
-// decoded exactly to bf16 in registers and the bf16 MFMA path is unchanged. ----
+// ---- Quantized weights: OCP FP8 E4M3 codes (one byte each) or OCP FP4 E2M1 codes (MXFP4:
+// two per byte, the even element in bits 0..3), with one E8M0 scale byte per 32 elements of
+// a row along K (the weight is code value * 2^(scale - 127)).  An E4M3 or E2M1 value times a
+// power of two is exactly a bf16 value (at most 3 mantissa bits, exponents in range), so the
+// weights are decoded exactly to bf16 in registers and the bf16 MFMA path is unchanged. ----
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // factor 2^(s - 127) of an E8M0 scale byte s (1..254)
@@ -67,13 +68,22 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t lo, uint32_t hi, float scale)
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// 8 E2M1 codes (dword w, element 0 in bits 0..3, element 7 in bits 28..31) times `scale`
+__device__ __forceinline__ bf16x8 decode8_fp4(uint32_t w, float scale) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Per-tile context shared by the row-count variants of the main loop.  Weight pointers
-// are byte pointers (2 bytes per bf16 weight, 1 per E4M3 code).
+// are byte pointers (2 bytes per bf16 weight, 1 per E4M3 code, 1/2 per E2M1 code).
 struct TileCtx {
     const uint16_t* A;    // activations (gate/up: token rows, gathered) or h (down)
     const uint8_t* bp0;   // this lane's first weight row (k offset applied)
     const uint8_t* bp1;   // second weight row block (up rows, or the next 16 down rows)
-    const uint8_t* sp0;   // E4M3: the scale rows of bp0's and bp1's rows
+    const uint8_t* sp0;   // quantized weights: the scale rows of bp0's and bp1's rows
     const uint8_t* sp1;
     int K, nk, top_k;     // reduction length, its 32-wide steps, routes per token
     bool gather;          // activation rows come from token rows via sorted_pairs
@@ -98,7 +108,7 @@ __device__ __forceinline__ const uint16_t* act_row(const TileCtx& c, int row) {
 // unconditional (clamped addresses): the steady state has no branches and the
 // compiler's memory-counter waits stay exact.  Thread t stages chunk (t + THREADS i)
 // mod (NRB*64), so smaller variants reload cached chunks instead of branching.
-template <bool GATED, bool W8, int NRB, int RING, int THREADS>
+template <bool GATED, int WF, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROWS * GKS], f32x4 (&acc)[NRB][2]) {
     constexpr int ACH = NRB * 64;                          // 16-byte activation chunks per step
     constexpr int AL = (ACH + THREADS - 1) / THREADS;      // activation loads per thread per step
@@ -115,7 +125,7 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     }
 
     u32x4 sa[AL], rb[RING][2];
-    uint32_t rs[RING][2];   // E4M3: the scale bytes of the step (one 32-k block)
+    uint32_t rs[RING][2];   // quantized weights: the scale bytes of the step (one 32-k block)
     const int nk = c.nk;
     auto clampk = [&](int kstep) { return (kstep < nk ? kstep : nk - 1) * GKS; };
     auto load_a = [&](int kstep) {
@@ -125,11 +135,16 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     };
     auto load_b = [&](int kstep, int set) {
         const int k0 = clampk(kstep);
-        if constexpr (W8) {
+        if constexpr (WF == WF_E4M3) {
             const uint2 w0 = *(const uint2*)(c.bp0 + k0);
             const uint2 w1 = *(const uint2*)(c.bp1 + k0);
             rb[set][0] = u32x4{w0.x, w0.y, 0u, 0u};
             rb[set][1] = u32x4{w1.x, w1.y, 0u, 0u};
+        } else if constexpr (WF == WF_E2M1) {
+            rb[set][0] = u32x4{*(const uint32_t*)(c.bp0 + k0 / 2), 0u, 0u, 0u};
+            rb[set][1] = u32x4{*(const uint32_t*)(c.bp1 + k0 / 2), 0u, 0u, 0u};
+        }
+        if constexpr (WF != WF_BF16) {
             rs[set][0] = c.sp0[k0 / 32];
             rs[set][1] = c.sp1[k0 / 32];
         } else {
@@ -138,8 +153,10 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
         }
     };
     auto wfrag = [&](int set, int blk) {
-        if constexpr (W8)
+        if constexpr (WF == WF_E4M3)
             return decode8(rb[set][blk][0], rb[set][blk][1], e8m0_factor(rs[set][blk]));
+        else if constexpr (WF == WF_E2M1)
+            return decode8_fp4(rb[set][blk][0], e8m0_factor(rs[set][blk]));
         else
             return __builtin_bit_cast(bf16x8, rb[set][blk]);
     };
@@ -205,29 +222,31 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
 }
 
 // Main loop for tiles of at most NRB <= 2 row blocks (decode-sized), where the weight
-// stream is the whole cost.  K advances 64 per step.  Each lane loads, per 16-row weight
-// block, the 16-byte chunks 2*(lane>>4) and 2*(lane>>4)+1 of a 128-byte window; the two
-// MFMAs of a step take the first and the second chunk (the activation operand uses the
-// same k order), so each pair of back-to-back loads reads whole 128-byte lines of 16
-// rows.  Weights run RING-1 steps ahead.  Activations are staged through LDS in chunks
-// of SKC columns for all rows of the tile (one barrier per chunk); the next chunk's
-// global loads are issued a whole chunk ahead.
+// stream is the whole cost.  A step covers one 128-byte line of every weight row (64 k of
+// bf16, 128 k of E4M3, 256 k of E2M1): lane (row, g = lane>>4) of a 16-row block loads
+// the 32 bytes at 32*g of its row's line with two 16-byte loads, so every load
+// instruction covers whole lines of 16 rows; the step's MFMAs take the lane's elements 8
+// at a time (the activation operand uses the same k order).  Weights run RING-1 steps
+// ahead.  Activations are staged through LDS in chunks of SKC columns for all rows of the
+// tile (one barrier per chunk); the next chunk's global loads are issued a whole chunk
+// ahead.
 constexpr int SKC = 512;            // activation columns per LDS chunk
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // LDS element offset of 16-byte chunk `ch` (0..SKC/8-1) of activation row `row`
 __device__ __forceinline__ int s_off(int row, int ch) { return row * SKC + ((ch ^ (row & 15)) << 3); }
 
-template <bool GATED, bool W8, int NRB, int RING, int THREADS>
+template <bool GATED, int WF, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
     constexpr int ROWS = NRB * 16;
     constexpr int ACH = ROWS * SKC / 8;          // 16-byte chunks per activation chunk
     constexpr int AL = ACH / THREADS;            // per thread
     static_assert(AL * THREADS == ACH, "activation chunk split");
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
-    // a step is one 128-byte line of each weight row: 64 k of bf16 or 128 k of E4M3 codes
-    constexpr int SW = W8 ? 128 : 64;
+    constexpr int WB = wbits(WF);
+    constexpr int SW = 1024 / WB;                // k per step: one 128-byte line per row
     constexpr int SKS_ = SKC / SW;               // steps per activation chunk
-    static_assert(SKS_ % RING == 0, "ring slots are static inside a chunk");
+    constexpr int U = RING / gcd_c(SKS_, RING);  // chunks per unrolled body: ring slots are static
     const int nk = c.K / SW;                     // steps
     const int nchunk = c.K / SKC;
     // activation staging of this thread
@@ -250,31 +269,28 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
         for (int i = 0; i < AL; ++i) *(u32x4*)(lds + buf * (ROWS * SKC) + alds[i]) = sa[i];
     };
-    // weights: in each step lane (row, g = lane>>4) of a 16-row block loads the 32 bytes at
-    // 32*g of its row's 128-byte line (two 16-byte loads), so every load instruction covers
-    // whole lines: the elements 16*g .. +15 of the step (bf16) or 32*g .. +31 (E4M3, exactly
-    // one 32-element scale block)
-    constexpr int BPE = W8 ? 1 : 2;
-    const uint8_t* b0 = c.bp0 + (lane >> 4) * (32 - 8 * BPE);
-    const uint8_t* b1 = c.bp1 + (lane >> 4) * (32 - 8 * BPE);
+    // weights: the 32 bytes at 32*g of the row's line hold the step's elements 16g .. +15
+    // (bf16), 32g .. +31 (E4M3: one 32-element scale block) or 64g .. +63 (E2M1: two blocks)
+    const uint8_t* b0 = c.bp0 + (lane >> 4) * (32 - WB);   // bp0 points at element 8g
+    const uint8_t* b1 = c.bp1 + (lane >> 4) * (32 - WB);
     u32x4 rb[RING][4];
     auto load_b = [&](int kstep, int set) {
-        const int k0 = (kstep < nk ? kstep : nk - 1) * SW * BPE;
+        const int k0 = (kstep < nk ? kstep : nk - 1) * 128;
         rb[set][0] = *(const u32x4*)(b0 + k0);
         rb[set][1] = *(const u32x4*)(b0 + k0 + 16);
         rb[set][2] = *(const u32x4*)(b1 + k0);
         rb[set][3] = *(const u32x4*)(b1 + k0 + 16);
     };
-    // E4M3 scales.  A chunk of SKC = 512 k is 16 scale bytes per row: byte 4j + g scales
-    // the codes of lane group g in step j.  Lane (row, g) loads the 16 bytes of chunk 4m + g
-    // (64 bytes per row per load, one load per row block for four chunks, one group ahead);
-    // at each chunk every lane fetches the 4 dwords of its chunk from lane (row, chunk & 3)
-    // with ds_bpermute and keeps byte g of dword j for step j.
+    // Scales of quantized weights.  A chunk of SKC = 512 k is 16 scale bytes per row.  Lane
+    // (row, g) loads the 16 bytes of chunk 4m + g (64 bytes per row per load, one load per
+    // row block for four chunks, one group ahead); at each chunk every lane fetches the 4
+    // dwords of its chunk from lane (row, chunk & 3) with ds_bpermute.  E4M3: byte 4j + g
+    // scales lane group g in step j; E2M1: bytes 8j + 2g and 8j + 2g + 1.
     const int ngrp = (nchunk + 3) >> 2;
     u32x4 sg[2] = {}, sgn[2] = {};
     uint32_t sc[2][4] = {};
     auto load_s = [&](int grp) {
-        if constexpr (W8) {
+        if constexpr (WF != WF_BF16) {
             const int m = grp < ngrp ? grp : ngrp - 1;
             int off = 64 * m + 16 * (lane >> 4);
             off = off < (c.K >> 5) - 16 ? off : (c.K >> 5) - 16;   // past the row's end: unused
@@ -283,7 +299,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         }
     };
     auto fetch_s = [&](int ck) {
-        if constexpr (W8) {
+        if constexpr (WF != WF_BF16) {
             const int src = ((lane & 15) + 16 * (ck & 3)) << 2;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
@@ -292,24 +308,40 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
                     sc[b][j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg[b][j]);
         }
     };
-    auto scale_of = [&](int blk, int j) { return e8m0_factor((sc[blk][j] >> (8 * (lane >> 4))) & 0xFFu); };
-    auto compute = [&](int kstep, int set, int buf) {
-        const int w = (kstep % SKS_) * (SW / 8);  // 16-byte chunk of the step inside the LDS chunk
+    // scale of block h (0, 1) of the lane's elements in step j of the chunk
+    auto scale_of = [&](int blk, int j, int h) {
+        if constexpr (WF == WF_E4M3) {
+            return e8m0_factor((sc[blk][j] >> (8 * (lane >> 4))) & 0xFFu);
+        } else {
+            const uint32_t d = (lane & 32) ? sc[blk][2 * j + 1] : sc[blk][2 * j];
+            return e8m0_factor((d >> (8 * (2 * ((lane >> 4) & 1) + h))) & 0xFFu);
+        }
+    };
+    // step j (0 .. SKS_-1, a compile-time constant in the unrolled loop) of the chunk in `buf`
+    auto compute = [&](int j, int set, int buf) {
+        const int w = j * (SW / 8);               // 16-byte chunk of the step inside the LDS chunk
         constexpr int NQ = SW / 32;               // MFMAs per block and step
-        float s0 = 0.f, s1 = 0.f;
-        if constexpr (W8) {
-            s0 = scale_of(0, kstep % SKS_);
-            s1 = scale_of(1, kstep % SKS_);
+        float s0[2] = {0.f, 0.f}, s1[2] = {0.f, 0.f};
+        if constexpr (WF != WF_BF16) {
+#pragma unroll
+            for (int h = 0; h < (WF == WF_E2M1 ? 2 : 1); ++h) {
+                s0[h] = scale_of(0, j, h);
+                s1[h] = scale_of(1, j, h);
+            }
         }
         // MFMA q of the step takes the lane's elements 8q .. 8q+7: chunk NQ*(lane>>4) + q
         // of the step's window
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             bf16x8 g, u;
-            if constexpr (W8) {
+            if constexpr (WF == WF_E4M3) {
                 const int l = q >> 1, h = q & 1;
-                g = decode8(rb[set][l][2 * h], rb[set][l][2 * h + 1], s0);
-                u = decode8(rb[set][2 + l][2 * h], rb[set][2 + l][2 * h + 1], s1);
+                g = decode8(rb[set][l][2 * h], rb[set][l][2 * h + 1], s0[0]);
+                u = decode8(rb[set][2 + l][2 * h], rb[set][2 + l][2 * h + 1], s1[0]);
+            } else if constexpr (WF == WF_E2M1) {
+                const int l = q >> 2;             // elements 32l .. 32l+31: scale block l
+                g = decode8_fp4(rb[set][l][q & 3], s0[l]);
+                u = decode8_fp4(rb[set][2 + l][q & 3], s1[l]);
             } else {
                 g = __builtin_bit_cast(bf16x8, rb[set][q]);
                 u = __builtin_bit_cast(bf16x8, rb[set][2 + q]);
@@ -337,35 +369,41 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();
-    for (int ck = 0; ck < nchunk; ++ck) {
-        const int buf = ck & 1;
-        if constexpr (W8) {
-            if ((ck & 3) == 0) {
-                sg[0] = sgn[0];
-                sg[1] = sgn[1];
-                load_s((ck >> 2) + 1);
-            }
-            fetch_s(ck);
-        }
+    for (int ck0 = 0; ck0 < nchunk; ck0 += U) {
 #pragma unroll
-        for (int j = 0; j < SKS_; ++j) {  // SKS_ is a multiple of RING: ring slots are static
-            const int kt = ck * SKS_ + j;
+        for (int u = 0; u < U; ++u) {
+            const int ck = ck0 + u;
+            if (U > 1 && ck >= nchunk) break;
+            const int buf = ck & 1;
+            if constexpr (WF != WF_BF16) {
+                if ((ck & 3) == 0) {
+                    sg[0] = sgn[0];
+                    sg[1] = sgn[1];
+                    load_s((ck >> 2) + 1);
+                }
+                fetch_s(ck);
+            }
+#pragma unroll
+            for (int j = 0; j < SKS_; ++j) {
+                const int kt = ck * SKS_ + j;
+                const int sl = u * SKS_ + j;      // static ring slot
+                __builtin_amdgcn_sched_barrier(0);
+                load_b(kt + RING - 1, (sl + RING - 1) % RING);
+                compute(j, sl % RING, buf);
+            }
+            // next chunk: stage it into the other buffer (read by no wave since the last
+            // barrier), then put the one after it in flight
             __builtin_amdgcn_sched_barrier(0);
-            load_b(kt + RING - 1, (j + RING - 1) % RING);
-            compute(kt, j % RING, buf);
+            store_a(buf ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(ck + 2);
+            lds_barrier();
         }
-        // next chunk: stage it into the other buffer (read by no wave since the last
-        // barrier), then put the one after it in flight
-        __builtin_amdgcn_sched_barrier(0);
-        store_a(buf ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(ck + 2);
-        lds_barrier();
     }
 }
 
 // Runs one tile: main loop variant, then the epilogue.
-template <bool GATED, bool W8, int NRB, int RING, int THREADS>
+template <bool GATED, int WF, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
     const int lane = threadIdx.x & 63;
     f32x4 acc[NRB][2];
@@ -373,11 +411,13 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (NRB <= 2) {
         if (c.K % SKC == 0)
-            tile_body_stream<GATED, W8, NRB, RING, THREADS>(c, &lds[0][0], acc);
+            // E2M1 (16 MFMAs per block and step): weights two steps ahead; a third register
+            // set spills
+            tile_body_stream<GATED, WF, NRB, WF == WF_E2M1 ? 3 : RING, THREADS>(c, &lds[0][0], acc);
         else
-            tile_body<GATED, W8, NRB, RING, THREADS>(c, lds, acc);
+            tile_body<GATED, WF, NRB, RING, THREADS>(c, lds, acc);
     } else
-        tile_body<GATED, W8, NRB, RING, THREADS>(c, lds, acc);
+        tile_body<GATED, WF, NRB, RING, THREADS>(c, lds, acc);
 
     // ---- epilogue (C layout of a 16x16 block: rows 4*(lane>>4)+q, column lane&15) ----
 #pragma unroll
@@ -399,7 +439,7 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     }
 }
 
-template <bool GATED, bool W8, int WAVES>
+template <bool GATED, int WF, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B1,
                      const uint8_t* __restrict__ S0, const uint8_t* __restrict__ S1, int K, int N, int top_k,
@@ -437,23 +477,23 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
     c.sorted_pairs = sorted_pairs;
     c.C = C;
     // weight rows of this wave (two 16-row MFMA operand blocks); byte pointers
-    constexpr int BPE = W8 ? 1 : 2;
+    constexpr int WB = wbits(WF);   // bits per weight
     int col0;
     if (GATED) {
         col0 = cblk * (WAVES * 16) + wave * 16;
         const int64_t r = (int64_t)e * N + col0 + (lane & 15);
-        c.bp0 = B0 + (r * K + (lane >> 4) * 8) * BPE;
-        c.bp1 = B1 + (r * K + (lane >> 4) * 8) * BPE;
-        if (W8) {
+        c.bp0 = B0 + (r * K + (lane >> 4) * 8) * WB / 8;
+        c.bp1 = B1 + (r * K + (lane >> 4) * 8) * WB / 8;
+        if (WF != WF_BF16) {
             c.sp0 = S0 + r * (K / 32);
             c.sp1 = S1 + r * (K / 32);
         }
     } else {
         col0 = cblk * (WAVES * 32) + wave * 32;
         const int64_t r = (int64_t)e * N + col0 + (lane & 15);
-        c.bp0 = B0 + (r * K + (lane >> 4) * 8) * BPE;
-        c.bp1 = c.bp0 + (int64_t)16 * K * BPE;
-        if (W8) {
+        c.bp0 = B0 + (r * K + (lane >> 4) * 8) * WB / 8;
+        c.bp1 = c.bp0 + (int64_t)16 * K * WB / 8;
+        if (WF != WF_BF16) {
             c.sp0 = S0 + r * (K / 32);
             c.sp1 = c.sp0 + (int64_t)16 * (K / 32);
         }
@@ -469,19 +509,19 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
 
     constexpr int TH = WAVES * 64;
     if (nrb > 16)
-        run_tile<GATED, W8, 18, 4, TH>(c, lds);
+        run_tile<GATED, WF, 18, 4, TH>(c, lds);
     else if (nrb > 12)
-        run_tile<GATED, W8, 16, 4, TH>(c, lds);
+        run_tile<GATED, WF, 16, 4, TH>(c, lds);
     else if (nrb > 8)
-        run_tile<GATED, W8, 12, 4, TH>(c, lds);
+        run_tile<GATED, WF, 12, 4, TH>(c, lds);
     else if (nrb > 4)
-        run_tile<GATED, W8, 8, 4, TH>(c, lds);
+        run_tile<GATED, WF, 8, 4, TH>(c, lds);
     else if (nrb > 2)
-        run_tile<GATED, W8, 4, 4, TH>(c, lds);
+        run_tile<GATED, WF, 4, 4, TH>(c, lds);
     else if (nrb > 1)
-        run_tile<GATED, W8, 2, 4, TH>(c, lds);
+        run_tile<GATED, WF, 2, 4, TH>(c, lds);
     else
-        run_tile<GATED, W8, 1, 4, TH>(c, lds);
+        run_tile<GATED, WF, 1, 4, TH>(c, lds);
 }
 
 // ---------------------------------------------------------------------------------
@@ -536,19 +576,24 @@ struct LineCtx {
 
 // Weight loads of step `kstep` of a work item into ring slot `set` (steps past the end
 // reload the last step, which the cache still holds).  bf16: two 16-byte chunks per block
-// (a whole 128-byte line per row); E4M3: one 16-byte load of the same 16 elements per lane
-// and the scale byte of their 32-k block.
-template <int NB, int RING, bool W8>
+// (a whole 128-byte line per row); E4M3: one 16-byte load of the same 16 elements per lane,
+// E2M1 one 8-byte load, and the scale byte of their 32-k block.
+template <int NB, int RING, int WF>
 __device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB],
                                             int b, int kstep, int set) {
     constexpr int HB = NB / 2;
-    constexpr int BPE = W8 ? 1 : 2;
+    constexpr int WB = wbits(WF);
     const int nk = c.K / WKS;
     const int ks = kstep < nk ? kstep : nk - 1;
-    const uint32_t so = (uint32_t)(ks * WKS * BPE) + (uint32_t)(b % HB) * (uint32_t)(16 * c.K * BPE);
+    const uint32_t so = (uint32_t)(ks * WKS * WB / 8) + (uint32_t)(b % HB) * (uint32_t)(16 * c.K * WB / 8);
     const __amdgpu_buffer_rsrc_t r = b < HB ? c.w0 : c.w1;
-    rb[set][b][0] = buf_load(r, c.wvoff, so);
-    if constexpr (W8) {
+    if constexpr (WF == WF_E2M1) {
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, c.wvoff, so, 0));
+        rb[set][b][0] = u32x4{v.x, v.y, 0u, 0u};
+    } else {
+        rb[set][b][0] = buf_load(r, c.wvoff, so);
+    }
+    if constexpr (WF != WF_BF16) {
         const uint32_t ss = (uint32_t)(ks * (WKS / 32)) + (uint32_t)(b % HB) * (uint32_t)(16 * (c.K / 32));
         rs[set][b] = __builtin_amdgcn_raw_buffer_load_b8(b < HB ? c.s0 : c.s1, c.svoff, ss, 0);
     } else {
@@ -557,16 +602,16 @@ __device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][
 }
 
 // The weights of a work item's first RING-1 steps.
-template <int NB, int RING, bool W8>
+template <int NB, int RING, int WF>
 __device__ __forceinline__ void line_prologue_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB]) {
 #pragma unroll
     for (int s2 = 0; s2 < RING - 1; ++s2)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) line_load_b<NB, RING, W8>(c, rb, rs, b, s2, s2);
+        for (int b = 0; b < NB; ++b) line_load_b<NB, RING, WF>(c, rb, rs, b, s2, s2);
 }
 
 // Main loop of one work item; the caller has issued its first RING-1 weight steps.
-template <int WAVES, int NB, int RING, int NRB, bool W8>
+template <int WAVES, int NB, int RING, int NRB, int WF>
 __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4 (&rb)[RING][NB][2],
                                           uint32_t (&rs)[RING][NB], f32x4 (&acc)[NRB][NB]) {
     constexpr int THREADS = WAVES * 64;
@@ -596,7 +641,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
     auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
     auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
-    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, W8>(c, rb, rs, b, kstep, set); };
+    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, WF>(c, rb, rs, b, kstep, set); };
     // fragment read offsets: row r*16 + (lane & 15), chunks 2g and 2g+1 (g = lane >> 4)
     const int fr = lane & 15, g = lane >> 4;
     const int off_e = w_off(fr, 2 * g);
@@ -623,14 +668,18 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
         const uint16_t* L = lds + (j & 1) * WBUF_ELEMS;
         const int wbuf = (j + 1) & 1;
         lds_barrier();
-        // this step's weight fragments (E4M3: decoded exactly to bf16)
+        // this step's weight fragments (quantized weights: decoded exactly to bf16)
         bf16x8 wf[NB][2];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            if constexpr (W8) {
+            if constexpr (WF == WF_E4M3) {
                 const float sc = e8m0_factor(rs[set][b]);
                 wf[b][0] = decode8(rb[set][b][0][0], rb[set][b][0][1], sc);
                 wf[b][1] = decode8(rb[set][b][0][2], rb[set][b][0][3], sc);
+            } else if constexpr (WF == WF_E2M1) {
+                const float sc = e8m0_factor(rs[set][b]);
+                wf[b][0] = decode8_fp4(rb[set][b][0][0], sc);
+                wf[b][1] = decode8_fp4(rb[set][b][0][1], sc);
             } else {
                 wf[b][0] = __builtin_bit_cast(bf16x8, rb[set][b][0]);
                 wf[b][1] = __builtin_bit_cast(bf16x8, rb[set][b][1]);
@@ -701,7 +750,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     }
 }
 
-template <bool GATED, bool W8, int WAVES, int NB, int RING>
+template <bool GATED, int WF, int WAVES, int NB, int RING>
 __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     const uint16_t* __restrict__ A, uint32_t a_bytes, const uint8_t* __restrict__ B0,
     const uint8_t* __restrict__ B1, const uint8_t* __restrict__ S0, const uint8_t* __restrict__ S1, int K, int N,
@@ -740,26 +789,26 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     c.row_count = te.row_count;
     c.gather = GATED;
     c.sorted_pairs = sorted_pairs;
-    constexpr int BPE = W8 ? 1 : 2;   // bytes per weight
-    c.wvoff = (uint32_t)(((lane & 15) * K + (lane >> 4) * 16) * BPE);
-    c.svoff = (uint32_t)((lane & 15) * (K / 32) + (lane >> 5));   // E4M3: block of elements 16*(lane>>4)
-    const uint32_t bytes = (uint32_t)(HB * 16 * K * BPE);
+    constexpr int WB = wbits(WF);   // bits per weight
+    c.wvoff = (uint32_t)(((lane & 15) * K + (lane >> 4) * 16) * WB / 8);
+    c.svoff = (uint32_t)((lane & 15) * (K / 32) + (lane >> 5));   // scale block of elements 16*(lane>>4)
+    const uint32_t bytes = (uint32_t)((int64_t)HB * 16 * K * WB / 8);
     const uint32_t sbytes = (uint32_t)(HB * 16 * (K / 32));
     int col0;
     int64_t r0, r1;   // first weight rows of the blocks of w0 and w1
     if (GATED) {
         col0 = cblk * (WAVES * HB * 16) + wave * (HB * 16);  // h columns [col0, col0 + 16*HB)
         r0 = r1 = e * N + col0;
-        c.w0 = make_rsrc(B0 + r0 * K * BPE, bytes);
-        c.w1 = make_rsrc(B1 + r1 * K * BPE, bytes);
+        c.w0 = make_rsrc(B0 + r0 * K * WB / 8, bytes);
+        c.w1 = make_rsrc(B1 + r1 * K * WB / 8, bytes);
     } else {
         col0 = cblk * (WAVES * NB * 16) + wave * (NB * 16);  // output columns [col0, col0 + 16*NB)
         r0 = e * N + col0;
         r1 = r0 + HB * 16;
-        c.w0 = make_rsrc(B0 + r0 * K * BPE, bytes);
-        c.w1 = make_rsrc(B0 + r1 * K * BPE, bytes);
+        c.w0 = make_rsrc(B0 + r0 * K * WB / 8, bytes);
+        c.w1 = make_rsrc(B0 + r1 * K * WB / 8, bytes);
     }
-    if (W8) {
+    if (WF != WF_BF16) {
         c.s0 = make_rsrc(S0 + r0 * (K / 32), sbytes);
         c.s1 = make_rsrc((GATED ? S1 : S0) + r1 * (K / 32), sbytes);
     }
@@ -768,13 +817,13 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
         constexpr int NRB = decltype(nrbc)::value;
         u32x4 rb[RING][NB][2];
         uint32_t rs[RING][NB];
-        line_prologue_b<NB, RING, W8>(c, rb, rs);
+        line_prologue_b<NB, RING, WF>(c, rb, rs);
         f32x4 acc[NRB][NB];
 #pragma unroll
         for (int r = 0; r < NRB; ++r)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        line_body<WAVES, NB, RING, NRB, W8>(c, lds, rb, rs, acc);
+        line_body<WAVES, NB, RING, NRB, WF>(c, lds, rb, rs, acc);
         // epilogue: each wave writes its bf16 columns of the tile into LDS (C layout of a
         // 16x16 block: rows 4*(lane>>4)+q, column lane&15), then the work-group stores
         // whole 16-byte chunks of every output row.  silu(g) = g / (1 + e^-g) with the
@@ -856,7 +905,7 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 #define DECODE_WAVES 4
 #endif
 
-template <bool GATED, bool W8>
+template <bool GATED, int WF>
 static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, const uint8_t* B1, const uint8_t* S0,
                         const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, const int32_t* sorted_pairs,
                         const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C,
@@ -864,7 +913,7 @@ static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, 
     if (P >= (int64_t)WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-        moe_gemm_line_kernel<GATED, W8, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
+        moe_gemm_line_kernel<GATED, WF, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
             A, (uint32_t)a_bytes, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
     } else {
         // decode-sized: 4-wave work-groups (two per compute unit) over half-width column
@@ -873,39 +922,50 @@ static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, 
         constexpr int W = DECODE_WAVES;
         const int ncb = N / (GATED ? W * 16 : W * 32);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-        moe_gemm_bf16_kernel<GATED, W8, W><<<(unsigned)blocks, W * 64, 0, s>>>(
+        moe_gemm_bf16_kernel<GATED, WF, W><<<(unsigned)blocks, W * 64, 0, s>>>(
             A, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
     }
 }
 
-hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, const uint8_t* s_gate,
-                          const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
+hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const void* w_up, int wf,
+                          const uint8_t* s_gate, const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
                           const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                           int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
+    if ((wf != WF_BF16) != (s_gate != nullptr)) return hipErrorInvalidValue;
     const uint16_t* A = (const uint16_t*)act;
     const uint8_t *B0 = (const uint8_t*)w_gate, *B1 = (const uint8_t*)w_up;
-    if (s_gate)
-        launch_gemm<true, true>(A, (uint64_t)T * H * 2, B0, B1, s_gate, s_up, H, I, top_k, T * top_k, E, sorted_pairs,
-                                tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
+    const uint64_t ab = (uint64_t)T * H * 2;
+    const int64_t P = T * top_k;
+    if (wf == WF_E4M3)
+        launch_gemm<true, WF_E4M3>(A, ab, B0, B1, s_gate, s_up, H, I, top_k, P, E, sorted_pairs, tiles, num_tiles,
+                                   max_tile_count, (uint16_t*)h, s);
+    else if (wf == WF_E2M1)
+        launch_gemm<true, WF_E2M1>(A, ab, B0, B1, s_gate, s_up, H, I, top_k, P, E, sorted_pairs, tiles, num_tiles,
+                                   max_tile_count, (uint16_t*)h, s);
     else
-        launch_gemm<true, false>(A, (uint64_t)T * H * 2, B0, B1, nullptr, nullptr, H, I, top_k, T * top_k, E,
-                                 sorted_pairs, tiles, num_tiles, max_tile_count, (uint16_t*)h, s);
+        launch_gemm<true, WF_BF16>(A, ab, B0, B1, nullptr, nullptr, H, I, top_k, P, E, sorted_pairs, tiles,
+                                   num_tiles, max_tile_count, (uint16_t*)h, s);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, const uint8_t* s_down, int64_t P, int H, int I,
-                       int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t P, int H,
+                       int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
+    if ((wf != WF_BF16) != (s_down != nullptr)) return hipErrorInvalidValue;
     const uint16_t* A = (const uint16_t*)h;
     const uint8_t* B0 = (const uint8_t*)w_down;
-    if (s_down)
-        launch_gemm<false, true>(A, (uint64_t)P * I * 2, B0, nullptr, s_down, nullptr, I, H, 0, P, E, sorted_pairs,
-                                 tiles, num_tiles, max_tile_count, (uint16_t*)y_pair, s);
+    const uint64_t ab = (uint64_t)P * I * 2;
+    if (wf == WF_E4M3)
+        launch_gemm<false, WF_E4M3>(A, ab, B0, nullptr, s_down, nullptr, I, H, 0, P, E, sorted_pairs, tiles,
+                                    num_tiles, max_tile_count, (uint16_t*)y_pair, s);
+    else if (wf == WF_E2M1)
+        launch_gemm<false, WF_E2M1>(A, ab, B0, nullptr, s_down, nullptr, I, H, 0, P, E, sorted_pairs, tiles,
+                                    num_tiles, max_tile_count, (uint16_t*)y_pair, s);
     else
-        launch_gemm<false, false>(A, (uint64_t)P * I * 2, B0, nullptr, nullptr, nullptr, I, H, 0, P, E, sorted_pairs,
-                                  tiles, num_tiles, max_tile_count, (uint16_t*)y_pair, s);
+        launch_gemm<false, WF_BF16>(A, ab, B0, nullptr, nullptr, nullptr, I, H, 0, P, E, sorted_pairs, tiles,
+                                    num_tiles, max_tile_count, (uint16_t*)y_pair, s);
     return hipGetLastError();
 }
 

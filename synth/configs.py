@@ -63,6 +63,11 @@ class Config:
     def P(self) -> int:
         return self.T * self.top_k
 
+    @property
+    def code_format(self) -> Optional[str]:
+        """The weight code format of a quantized config ("e4m3", "e2m1"), else None."""
+        return {"fp8": "e4m3", "mxfp4": "e2m1"}.get(self.weights)
+
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
 

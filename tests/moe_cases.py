@@ -68,7 +68,8 @@ def run_forward(cfg: Config, d: DeviceInputs, timer=None):
     moe_y = torch.empty((cfg.T, cfg.H), dtype=act_dt, device="cuda") if cfg.sublayer else None
     sub = bm.sublayer(d.g1, d.g2, cfg.eps, cfg.residual_k) if cfg.sublayer else None
     bm.forward(shape, d.x, d.wr, d.bias, d.wg, d.wu, d.wd, out, ws, sublayer=sub, topk_idx=idx, topk_w=w,
-               moe_y=moe_y, stage_events=timer.events if timer else None, w_scales=d.w_scales)
+               moe_y=moe_y, stage_events=timer.events if timer else None, w_scales=d.w_scales,
+               w_format=cfg.code_format or "e4m3")
     torch.cuda.synchronize()
     return dict(out=host(out), idx=host(idx), w=host(w), moe_y=host(moe_y) if moe_y is not None else None)
 
@@ -147,6 +148,18 @@ MID_CASES = {
     "mid_fp8_decode_h2560_t12": mid_config("mid_fp8_decode_h2560_t12", 12, H=2560, I=1536, E=16, n_group=4,
                                            topk_group=2, top_k=4, weights="fp8", wr_std=math.sqrt(1.0 / 2560),
                                            seed_base=26000),
+    # 4-bit expert weights (MXFP4: E2M1 codes two per byte + E8M0 block scales): the line
+    # kernel's 8-byte loads, the decode kernel's 256-k stream steps (gate/up, one chunk at
+    # K = 512, five at K = 2560), its 32-k steps (down, K = 256) and its large-tile loop
+    "mid_mxfp4_prefill_t1000": mid_config("mid_mxfp4_prefill_t1000", 1000, weights="mxfp4", seed_base=27000),
+    "mid_mxfp4_decode_t24": mid_config("mid_mxfp4_decode_t24", 24, weights="mxfp4", seed_base=28000),
+    "mid_mxfp4_skew_decode_t48": mid_config("mid_mxfp4_skew_decode_t48", 48, bias="zipf:0.6", weights="mxfp4",
+                                            seed_base=29000),
+    "mid_mxfp4_sublayer_t333": mid_config("mid_mxfp4_sublayer_t333", 333, sublayer=True, residual_k=40,
+                                          weights="mxfp4", seed_base=30000),
+    "mid_mxfp4_decode_h2560_t12": mid_config("mid_mxfp4_decode_h2560_t12", 12, H=2560, I=1536, E=16, n_group=4,
+                                             topk_group=2, top_k=4, weights="mxfp4", wr_std=math.sqrt(1.0 / 2560),
+                                             seed_base=31000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }

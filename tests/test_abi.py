@@ -114,27 +114,28 @@ def test_forward_validation_happens_before_launch():
     assert _raw_forward(s0, bm.workspace_size(s0, bm.OP_FORWARD)) == bm.BEAM_OK
 
 
-def _raw_forward_fp8(shape, ws_bytes, scales=(FAKE, FAKE, FAKE), w=FAKE):
-    f = bm.lib().beam_moe_forward_fp8
+def _raw_forward_fp8(shape, ws_bytes, scales=(FAKE, FAKE, FAKE), w=FAKE, entry="beam_moe_forward_fp8"):
+    f = getattr(bm.lib(), entry)
     return f(ctypes.byref(shape), FAKE, FAKE, FAKE, w, FAKE, FAKE, scales[0], scales[1], scales[2], None, FAKE, None,
              None, None, FAKE if ws_bytes else None, ws_bytes, None, None)
 
 
-def test_forward_fp8_validation_happens_before_launch():
+@pytest.mark.parametrize("entry", ["beam_moe_forward_fp8", "beam_moe_forward_mxfp4"])
+def test_forward_quantized_validation_happens_before_launch(entry):
     s = _beam(T=64)
     need = bm.workspace_size(s, bm.OP_FORWARD)   # the same workspace as the bf16 forward
-    assert _raw_forward_fp8(s, need - 1) == bm.BEAM_ERR_WORKSPACE
+    assert _raw_forward_fp8(s, need - 1, entry=entry) == bm.BEAM_ERR_WORKSPACE
     for i in range(3):   # every scale tensor is required
         sc = [FAKE, FAKE, FAKE]
         sc[i] = None
-        assert _raw_forward_fp8(s, need, scales=tuple(sc)) == bm.BEAM_ERR_INVALID_ARG
-    assert _raw_forward_fp8(s, need, scales=(FAKE, FAKE + 4, FAKE)) == bm.BEAM_ERR_INVALID_ARG   # misaligned
-    assert _raw_forward_fp8(s, need, w=None) == bm.BEAM_ERR_INVALID_ARG
-    assert _raw_forward_fp8(s, need, w=FAKE + 8) == bm.BEAM_ERR_INVALID_ARG   # codes are read 16 bytes at a time
+        assert _raw_forward_fp8(s, need, scales=tuple(sc), entry=entry) == bm.BEAM_ERR_INVALID_ARG
+    assert _raw_forward_fp8(s, need, scales=(FAKE, FAKE + 4, FAKE), entry=entry) == bm.BEAM_ERR_INVALID_ARG
+    assert _raw_forward_fp8(s, need, w=None, entry=entry) == bm.BEAM_ERR_INVALID_ARG
+    assert _raw_forward_fp8(s, need, w=FAKE + 8, entry=entry) == bm.BEAM_ERR_INVALID_ARG   # 16-byte loads
     sf = _beam(T=64, H=256, I=128, dtype="f32")
-    assert _raw_forward_fp8(sf, bm.workspace_size(sf, bm.OP_FORWARD)) == bm.BEAM_ERR_UNSUPPORTED
+    assert _raw_forward_fp8(sf, bm.workspace_size(sf, bm.OP_FORWARD), entry=entry) == bm.BEAM_ERR_UNSUPPORTED
     s0 = _beam(T=0)
-    assert _raw_forward_fp8(s0, 0) == bm.BEAM_OK
+    assert _raw_forward_fp8(s0, 0, entry=entry) == bm.BEAM_OK
 
 
 def test_route_permute_rmsnorm_validation():

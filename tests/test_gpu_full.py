@@ -1,7 +1,8 @@
 """GPU parity at the full Beam shapes (H=5120, E=256, I=2560; 20 GB of bf16 expert weights),
 in the launch configuration the benchmark times, at two serving shapes between decode and
 prefill (256 and 1024 tokens: 8 and 32 routed rows per expert, on either side of the kernel
-switch), and for decode and prefill with the weights in 8-bit storage (E4M3 + E8M0 scales).
+switch), and for decode and prefill with the weights in 8-bit (E4M3) and 4-bit (MXFP4: E2M1)
+storage with E8M0 scales per 32 weights.
 
 Routing is compared bit-exact (as sets) on ALL tokens; outputs are compared on a seeded
 sample of 256 tokens plus, for every non-empty expert, the tokens of its first and last
@@ -13,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from synth.configs import CONFIGS, expert_weights, fp8_weights, make_inputs
+from synth.configs import CONFIGS, expert_weights, fp8_weights, make_inputs, mxfp4_weights
 
 from moe_cases import as_f64, assert_routing_equal, dev, host, rel_err, shape_of
 
@@ -35,6 +36,22 @@ def weights():
     print("\nweights: generated in %.1fs, uploaded in %.1fs" % (t1 - t0, time.time() - t1), flush=True)
     yield hw, dw
     del dw
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def weights_mxfp4(weights):
+    """The same weights in 4-bit storage (E2M1 codes two per byte + E8M0 block scales)."""
+    import torch
+    hw, _ = weights
+    t0 = time.time()
+    hq, scales = mxfp4_weights(hw)
+    dq = tuple(dev(a) for a in hq)
+    ds = tuple(dev(a) for a in scales)
+    torch.cuda.synchronize()
+    print("\nmxfp4 weights: quantized and uploaded in %.1fs" % (time.time() - t0), flush=True)
+    yield hq, scales, dq, ds
+    del dq, ds
     torch.cuda.empty_cache()
 
 
@@ -71,13 +88,14 @@ def _sample(cfg, idx, extra_cap=512):
 
 
 @pytest.mark.parametrize("name", ["decode_t64", "serve_t256", "serve_t1024", "skew_t6000", "prefill_t8192",
-                                  "sublayer_t32768", "decode_t64_fp8", "prefill_t8192_fp8"])
+                                  "sublayer_t32768", "decode_t64_fp8", "prefill_t8192_fp8", "decode_t64_mxfp4",
+                                  "prefill_t8192_mxfp4"])
 def test_full_shape_layer(name, request):
     import torch
     import sparse_moe_layer_04_amd as bm
     cfg = CONFIGS[name]
-    if cfg.weights == "fp8":
-        hw, w_scales, dw, d_scales = request.getfixturevalue("weights_fp8")
+    if cfg.weights != "bf16":
+        hw, w_scales, dw, d_scales = request.getfixturevalue("weights_" + cfg.weights)
     else:
         hw, dw = request.getfixturevalue("weights")
         w_scales = d_scales = None
@@ -103,7 +121,7 @@ def test_full_shape_layer(name, request):
         g1, g2 = dev(inp.pre_gain), dev(inp.post_gain)
         sub = bm.sublayer(g1, g2, cfg.eps, cfg.residual_k)
     bm.forward(shape, x, dw[0], dev(inp.bias), dw[1], dw[2], dw[3], out, ws, sublayer=sub, topk_idx=idx, topk_w=w,
-               moe_y=moe_y, w_scales=d_scales)
+               moe_y=moe_y, w_scales=d_scales, w_format=cfg.code_format or "e4m3")
     torch.cuda.synchronize()
     g_idx, g_w = host(idx), host(w)
     assert_routing_equal(g_idx, g_w, r.idx, r.w, cfg.rho)
