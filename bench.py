@@ -283,7 +283,7 @@ def main():
                     choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768", "decode_t64_fp8",
                              "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4"])
     ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
-    ap.add_argument("--cpu-tokens", type=int, default=1536, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the decode and prefill layers with 8-bit and 4-bit expert weights")
