@@ -34,9 +34,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(EXPERTS_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(text=None) -> str:
+    """Hash of the expert-GEMM source with its comments and blank space removed, so that a
+    change to the comments alone keeps recorded counter traffic valid."""
+    import re
+    if text is None:
+        with open(EXPERTS_SRC) as f:
+            text = f.read()
+    code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def weight_bytes_per_element(cfg):
@@ -83,7 +91,7 @@ def load_traffic(workload, kernel):
         with open(TRAFFIC_JSON) as f:
             d = json.load(f)
         ent = d[workload]
-        if ent.get("experts_hip_sha256_16") != kernel_source_hash():
+        if ent.get("experts_hip_code_sha256_16") != kernel_source_hash():
             return None
         k = ent[kernel]
         return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
@@ -119,7 +127,7 @@ def ingest_counters(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write
     f_fetch, f_write = n / cf, n / cw
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
-    ent = {"experts_hip_sha256_16": kernel_source_hash(),
+    ent = {"experts_hip_code_sha256_16": kernel_source_hash(),
            "calibration": {"copy_bytes": n, "fetch_factor": f_fetch, "write_factor": f_write}}
     for key, name in KERNEL_NAMES.items():
         kf = [v for k, v in fetch.items() if "moe_gemm" in k and name in k]

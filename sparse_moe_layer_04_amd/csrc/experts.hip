@@ -9,7 +9,8 @@
 // where row r of the expert-sorted pair list holds pair p = t*top_k + j routed to e.
 //
 // bf16 path (details below): one work-group computes one (tile, column block) on
-// MFMA.  Gate/up column blocks hold the gate and the up rows of the same output
+// bf16 MFMA.  Expert weights are bf16, or E4M3 / E2M1 codes with E8M0 block scales that
+// are decoded exactly to bf16 in registers (template parameter WF).  Gate/up column blocks hold the gate and the up rows of the same output
 // columns, so the SwiGLU epilogue has both operands in registers.  The gate/up A
 // operand is gathered straight from the token rows (no permuted copy); the down
 // epilogue scatters each row to its pair position.
@@ -100,7 +101,8 @@ __device__ __forceinline__ const uint16_t* act_row(const TileCtx& c, int row) {
     return c.A + r * c.K;
 }
 
-// Main loop for tiles of at most NRB 16-row blocks (NRB >= 4).  Activations go
+// Main loop for tiles of at most NRB 16-row blocks (the decode-sized NRB <= 2 take the
+// streaming loop below when K is a multiple of its chunk).  Activations go
 // through an LDS double buffer: one register set stages step kt+2 while step kt+1 is
 // written to LDS and step kt is multiplied; weights stream RING-1 steps ahead.  Within
 // a step the loads are issued activations first, then weights, so waiting for the
@@ -566,10 +568,10 @@ struct LineCtx {
     __amdgpu_buffer_rsrc_t act;   // activation tensor (token rows or h rows)
     __amdgpu_buffer_rsrc_t w0;    // weight blocks [0, NB/2)
     __amdgpu_buffer_rsrc_t w1;    // weight blocks [NB/2, NB)
-    __amdgpu_buffer_rsrc_t s0;    // E4M3: scale rows of the blocks of w0
+    __amdgpu_buffer_rsrc_t s0;    // quantized weights: scale rows of the blocks of w0
     __amdgpu_buffer_rsrc_t s1;    //       and of w1
     uint32_t wvoff;               // this lane's byte offset inside a weight block
-    uint32_t svoff;               // E4M3: this lane's byte offset inside a block's scale rows
+    uint32_t svoff;               // quantized weights: this lane's byte offset inside a block's scale rows
     int K, top_k, row_begin, row_count;
     bool gather;
     const int32_t* sorted_pairs;
