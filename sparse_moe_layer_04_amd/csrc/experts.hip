@@ -231,16 +231,25 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
 // at a time (the activation operand uses the same k order).  Weights run RING-1 steps
 // ahead.  Activations are staged through LDS in chunks of SKC columns for all rows of the
 // tile (one barrier per chunk); the next chunk's global loads are issued a whole chunk
-// ahead.
-constexpr int SKC = 512;            // activation columns per LDS chunk
+// ahead.  Quantized weights: each wave copies the scale rows of its two blocks (16 rows x
+// K/32 bytes each, contiguous in memory) into its own LDS area once per tile with whole-line
+// loads, and reads the 16 scale bytes of a row and chunk from there.
+constexpr int SKC = 512;            // activation columns per LDS chunk (tiles of 16 rows)
+constexpr int SKC2 = 256;           // ... of 32 rows (the same LDS bytes)
+constexpr int SACT_ELEMS = 2 * 16 * SKC;   // the double-buffered activation chunks
+constexpr int SCALE_KMAX = 8192;    // longest K whose scale rows fit the per-wave LDS area
+constexpr int SCALE_WAVE_BYTES = 2 * 16 * (SCALE_KMAX / 32);
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-// LDS element offset of 16-byte chunk `ch` (0..SKC/8-1) of activation row `row`
-__device__ __forceinline__ int s_off(int row, int ch) { return row * SKC + ((ch ^ (row & 15)) << 3); }
+// LDS element offset of 16-byte chunk `ch` (0..C/8-1) of activation row `row` (C columns per row)
+template <int C>
+__device__ __forceinline__ int s_off(int row, int ch) { return row * C + ((ch ^ (row & 15)) << 3); }
 
 template <bool GATED, int WF, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
     constexpr int ROWS = NRB * 16;
+    constexpr int SKC = NRB <= 1 ? beam::SKC : SKC2;
+    static_assert(2 * ROWS * SKC <= SACT_ELEMS, "activation chunks fit their LDS area");
     constexpr int ACH = ROWS * SKC / 8;          // 16-byte chunks per activation chunk
     constexpr int AL = ACH / THREADS;            // per thread
     static_assert(AL * THREADS == ACH, "activation chunk split");
@@ -259,7 +268,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         const int q = tid + i * THREADS;
         const int row = q / (SKC / 8), ch = q % (SKC / 8);
         ap[i] = act_row(c, row) + ch * 8;
-        alds[i] = s_off(row, ch);
+        alds[i] = s_off<SKC>(row, ch);
     }
     u32x4 sa[AL];
     auto load_a = [&](int chunk) {
@@ -283,31 +292,52 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         rb[set][2] = *(const u32x4*)(b1 + k0);
         rb[set][3] = *(const u32x4*)(b1 + k0 + 16);
     };
-    // Scales of quantized weights.  A chunk of SKC = 512 k is 16 scale bytes per row.  Lane
-    // (row, g) loads the 16 bytes of chunk 4m + g (64 bytes per row per load, one load per
-    // row block for four chunks, one group ahead); at each chunk every lane fetches the 4
-    // dwords of its chunk from lane (row, chunk & 3) with ds_bpermute.  E4M3: byte 4j + g
-    // scales lane group g in step j; E2M1: bytes 8j + 2g and 8j + 2g + 1.
-    const int ngrp = (nchunk + 3) >> 2;
-    u32x4 sg[2] = {}, sgn[2] = {};
+    // Scales of quantized weights: a row's chunk of 512 k has 16 scale bytes (32 at 32-row
+    // tiles' 256-k chunks, 8).  E4M3: byte 4j + g scales lane group g in step j; E2M1: bytes
+    // 8j + 2g and 8j + 2g + 1.  The wave's two blocks' scale rows sit in its LDS area (row r
+    // of block b at b*16*K/32 + r*K/32); sc holds the lane's row's bytes of the current chunk.
+    constexpr int SCB = SKC / 32;                       // scale bytes per row and chunk
+    uint8_t* sarea = reinterpret_cast<uint8_t*>(lds + SACT_ELEMS) + (threadIdx.x >> 6) * SCALE_WAVE_BYTES;
     uint32_t sc[2][4] = {};
-    auto load_s = [&](int grp) {
+    // the whole scale rows of the wave's blocks, once per tile: loaded into registers first
+    // (their latency overlaps the first activation chunk's), then written to the LDS area
+    constexpr int SLD = WF == WF_BF16 ? 1 : SCALE_KMAX / 2 / 1024;   // 16-byte loads per lane and block
+    u32x4 st[2][SLD];
+    auto stage_s_load = [&]() {
         if constexpr (WF != WF_BF16) {
-            const int m = grp < ngrp ? grp : ngrp - 1;
-            int off = 64 * m + 16 * (lane >> 4);
-            off = off < (c.K >> 5) - 16 ? off : (c.K >> 5) - 16;   // past the row's end: unused
-            sgn[0] = *(const u32x4*)(c.sp0 + off);
-            sgn[1] = *(const u32x4*)(c.sp1 + off);
+            const int nb = c.K >> 1;                        // bytes per block: 16 rows x K/32
+            const uint8_t* src[2] = {c.sp0 - (lane & 15) * (c.K >> 5), c.sp1 - (lane & 15) * (c.K >> 5)};
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < SLD; ++i)
+                    if (16 * lane + 1024 * i < nb) st[b][i] = *(const u32x4*)(src[b] + 16 * lane + 1024 * i);
+        }
+    };
+    auto stage_s_store = [&]() {
+        if constexpr (WF != WF_BF16) {
+            const int nb = c.K >> 1;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < SLD; ++i)
+                    if (16 * lane + 1024 * i < nb) *(u32x4*)(sarea + b * nb + 16 * lane + 1024 * i) = st[b][i];
         }
     };
     auto fetch_s = [&](int ck) {
         if constexpr (WF != WF_BF16) {
-            const int src = ((lane & 15) + 16 * (ck & 3)) << 2;
+            const int o = (lane & 15) * (c.K >> 5) + ck * SCB;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sc[b][j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg[b][j]);
+            for (int b = 0; b < 2; ++b) {
+                const uint8_t* p = sarea + b * (c.K >> 1) + o;
+                if constexpr (SCB == 16) {
+                    const u32x4 v = *(const u32x4*)p;
+                    sc[b][0] = v[0], sc[b][1] = v[1], sc[b][2] = v[2], sc[b][3] = v[3];
+                } else {
+                    const uint2 v = *(const uint2*)p;
+                    sc[b][0] = v.x, sc[b][1] = v.y;
+                }
+            }
         }
     };
     // scale of block h (0, 1) of the lane's elements in step j of the chunk
@@ -351,7 +381,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
                 const bf16x8 a = *(const bf16x8*)(lds + buf * (ROWS * SKC) +
-                                                  s_off(r * 16 + (lane & 15), w + NQ * (lane >> 4) + q));
+                                                  s_off<SKC>(r * 16 + (lane & 15), w + NQ * (lane >> 4) + q));
                 acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g, acc[r][0], 0, 0, 0);
                 acc[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u, acc[r][1], 0, 0, 0);
             }
@@ -359,12 +389,14 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     };
     // prologue: chunk 0 into LDS, chunk 1 in flight, weights RING-1 steps ahead (issuing the
     // weights before the activation lookups measured no faster)
+    stage_s_load();
+    __builtin_amdgcn_sched_barrier(0);
     load_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_s_store();
     store_a(0);
     __builtin_amdgcn_sched_barrier(0);
     load_a(1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_s(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < RING - 1; ++s) {
@@ -378,14 +410,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
             const int ck = ck0 + u;
             if (U > 1 && ck >= nchunk) break;
             const int buf = ck & 1;
-            if constexpr (WF != WF_BF16) {
-                if ((ck & 3) == 0) {
-                    sg[0] = sgn[0];
-                    sg[1] = sgn[1];
-                    load_s((ck >> 2) + 1);
-                }
-                fetch_s(ck);
-            }
+            fetch_s(ck);
 #pragma unroll
             for (int j = 0; j < SKS_; ++j) {
                 const int kt = ck * SKS_ + j;
@@ -413,7 +438,8 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
 #pragma unroll
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (NRB <= 2) {
-        if (c.K % SKC == 0)
+        constexpr int CHUNK = NRB <= 1 ? SKC : SKC2;   // the streaming loop's activation chunk
+        if (c.K % CHUNK == 0 && (WF == WF_BF16 || c.K <= SCALE_KMAX))
             // E2M1 (16 MFMAs per block and step): weights one step ahead (two steps ahead
             // measured no faster; three spill)
             tile_body_stream<GATED, WF, NRB, WF == WF_E2M1 ? 2 : RING, THREADS>(c, &lds[0][0], acc);
@@ -448,7 +474,10 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
                      const uint8_t* __restrict__ S0, const uint8_t* __restrict__ S1, int K, int N, int top_k,
                      const int32_t* __restrict__ sorted_pairs, const TileEntry* __restrict__ tiles,
                      const int32_t* __restrict__ num_tiles, int n_col_blocks, uint16_t* __restrict__ C) {
-    constexpr int LDS_ELEMS = 2 * GROWS * GKS > 2 * 32 * SKC ? 2 * GROWS * GKS : 2 * 32 * SKC;
+    // the large-tile loop's buffers, or the streaming loop's activation chunks and the
+    // waves' scale areas
+    constexpr int STREAM_ELEMS = SACT_ELEMS + WAVES * SCALE_WAVE_BYTES / 2;
+    constexpr int LDS_ELEMS = 2 * GROWS * GKS > STREAM_ELEMS ? 2 * GROWS * GKS : STREAM_ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t lds_raw[LDS_ELEMS];
     auto lds = reinterpret_cast<uint16_t (*)[GROWS * GKS]>(lds_raw);
 

@@ -160,6 +160,17 @@ MID_CASES = {
     "mid_mxfp4_decode_h2560_t12": mid_config("mid_mxfp4_decode_h2560_t12", 12, H=2560, I=1536, E=16, n_group=4,
                                              topk_group=2, top_k=4, weights="mxfp4", wr_std=math.sqrt(1.0 / 2560),
                                              seed_base=31000),
+    # 17-32 rows in some experts: the streaming loop's 32-row tiles (256-column activation
+    # chunks; with quantized weights, chunks of 8 scale bytes per row), at K = 512 / 256 and,
+    # with several chunks, at K = 2560 / 1536
+    "mid_mxfp4_skew_decode_t32": mid_config("mid_mxfp4_skew_decode_t32", 32, bias="zipf:0.6", weights="mxfp4",
+                                            seed_base=32000),
+    "mid_fp8_skew_h2560_t28": mid_config("mid_fp8_skew_h2560_t28", 28, H=2560, I=1536, E=16, n_group=4,
+                                         topk_group=2, top_k=4, bias="zipf:0.6", weights="fp8",
+                                         wr_std=math.sqrt(1.0 / 2560), seed_base=34000),
+    "mid_mxfp4_skew_h2560_t28": mid_config("mid_mxfp4_skew_h2560_t28", 28, H=2560, I=1536, E=16, n_group=4,
+                                           topk_group=2, top_k=4, bias="zipf:0.6", weights="mxfp4",
+                                           wr_std=math.sqrt(1.0 / 2560), seed_base=34000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }
