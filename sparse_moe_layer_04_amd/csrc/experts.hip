@@ -927,11 +927,17 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
     return bf16 ? GROWS : (1 << 30);  // the fp32 path does not use tiles
 }
 
-// Average rows per expert from which the line-streaming kernel is used.  Below it the
-// decode kernel (4-wave work-groups, two per CU) is 1-2% faster; above it the line kernel
-// wins, by 25% at 32-48 rows per expert (measured over 16..8192 tokens of the Beam layer).
+// Average rows per expert from which the line-streaming kernel is used.  bf16: below it
+// the decode kernel (4-wave work-groups, two per CU) is 1-2% faster; above it the line
+// kernel wins, by 25% at 32-48 rows per expert (measured over 16..8192 tokens of the Beam
+// layer).  Quantized weights: the line kernel reads them in half or quarter lines, and the
+// decode kernel stays ahead up to 20 rows per expert (by 33-55% at 8, 9-23% at 20); the line
+// kernel wins from 24.
 #ifndef WIDE_MIN_ROWS_PER_EXPERT
 #define WIDE_MIN_ROWS_PER_EXPERT 8
+#endif
+#ifndef WIDE_MIN_ROWS_PER_EXPERT_QUANT
+#define WIDE_MIN_ROWS_PER_EXPERT_QUANT 24
 #endif
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4
@@ -942,7 +948,8 @@ static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, 
                         const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, const int32_t* sorted_pairs,
                         const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C,
                         hipStream_t s) {
-    if (P >= (int64_t)WIDE_MIN_ROWS_PER_EXPERT * E && K % (2 * WKS) == 0) {
+    constexpr int wide_min = WF == WF_BF16 ? WIDE_MIN_ROWS_PER_EXPERT : WIDE_MIN_ROWS_PER_EXPERT_QUANT;
+    if (P >= (int64_t)wide_min * E && K % (2 * WKS) == 0) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
         moe_gemm_line_kernel<GATED, WF, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(

@@ -96,9 +96,14 @@ CONFIGS = {
                                **_BEAM),
     "prefill_t8192_mxfp4": Config("prefill_t8192_mxfp4", T=8192, bias="zero", seed_base=2000, weights="mxfp4",
                                   **_BEAM),
+    # serving shape with quantized weights: 16 rows per expert, below their kernel switch
+    "serve_t512_fp8": Config("serve_t512_fp8", T=512, bias="uniform:0.05", seed_base=7000, weights="fp8", **_BEAM),
+    "serve_t512_mxfp4": Config("serve_t512_mxfp4", T=512, bias="uniform:0.05", seed_base=7000, weights="mxfp4",
+                               **_BEAM),
 }
 CONFIG_ORDER = ["tiny_f32", "decode_t64", "prefill_t8192", "skew_t6000", "sublayer_t32768", "serve_t256",
-                "serve_t1024", "decode_t64_fp8", "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4"]
+                "serve_t1024", "decode_t64_fp8", "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4",
+                "serve_t512_fp8", "serve_t512_mxfp4"]
 
 
 def seed_index(name: str) -> int:

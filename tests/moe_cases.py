@@ -171,6 +171,10 @@ MID_CASES = {
     "mid_mxfp4_skew_h2560_t28": mid_config("mid_mxfp4_skew_h2560_t28", 28, H=2560, I=1536, E=16, n_group=4,
                                            topk_group=2, top_k=4, bias="zipf:0.6", weights="mxfp4",
                                            wr_std=math.sqrt(1.0 / 2560), seed_base=34000),
+    # 8-bit and 4-bit weights at 20 rows per expert: below the quantized formats' kernel
+    # switch (24), so the decode kernel with tiles of every size
+    "mid_fp8_serve_t160": mid_config("mid_fp8_serve_t160", 160, weights="fp8", seed_base=35000),
+    "mid_mxfp4_serve_t160": mid_config("mid_mxfp4_serve_t160", 160, weights="mxfp4", seed_base=36000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }

@@ -89,7 +89,7 @@ def _sample(cfg, idx, extra_cap=512):
 
 @pytest.mark.parametrize("name", ["decode_t64", "serve_t256", "serve_t1024", "skew_t6000", "prefill_t8192",
                                   "sublayer_t32768", "decode_t64_fp8", "prefill_t8192_fp8", "decode_t64_mxfp4",
-                                  "prefill_t8192_mxfp4"])
+                                  "prefill_t8192_mxfp4", "serve_t512_fp8", "serve_t512_mxfp4"])
 def test_full_shape_layer(name, request):
     import torch
     import sparse_moe_layer_04_amd as bm
