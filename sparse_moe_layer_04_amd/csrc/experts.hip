@@ -235,7 +235,8 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
 // K/32 bytes each, contiguous in memory) into its own LDS area once per tile with whole-line
 // loads, and reads the 16 scale bytes of a row and chunk from there.
 constexpr int SKC = 512;            // activation columns per LDS chunk (tiles of 16 rows)
-constexpr int SKC2 = 256;           // ... of 32 rows (the same LDS bytes)
+// activation columns per chunk for tiles of NRB row blocks: the same LDS bytes at every size
+__host__ __device__ constexpr int stream_chunk(int nrb) { return nrb <= 1 ? 512 : nrb <= 2 ? 256 : 128; }
 constexpr int SACT_ELEMS = 2 * 16 * SKC;   // the double-buffered activation chunks
 constexpr int SCALE_KMAX = 8192;    // longest K whose scale rows fit the per-wave LDS area
 constexpr int SCALE_WAVE_BYTES = 2 * 16 * (SCALE_KMAX / 32);
@@ -248,7 +249,7 @@ __device__ __forceinline__ int s_off(int row, int ch) { return row * C + ((ch ^ 
 template <bool GATED, int WF, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
     constexpr int ROWS = NRB * 16;
-    constexpr int SKC = NRB <= 1 ? beam::SKC : SKC2;
+    constexpr int SKC = stream_chunk(NRB);
     static_assert(2 * ROWS * SKC <= SACT_ELEMS, "activation chunks fit their LDS area");
     constexpr int ACH = ROWS * SKC / 8;          // 16-byte chunks per activation chunk
     constexpr int AL = ACH / THREADS;            // per thread
@@ -257,6 +258,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     constexpr int WB = wbits(WF);
     constexpr int SW = 1024 / WB;                // k per step: one 128-byte line per row
     constexpr int SKS_ = SKC / SW;               // steps per activation chunk
+    static_assert(SKS_ >= 1, "a chunk holds at least one step");
     constexpr int U = RING / gcd_c(SKS_, RING);  // chunks per unrolled body: ring slots are static
     const int nk = c.K / SW;                     // steps
     const int nchunk = c.K / SKC;
@@ -292,8 +294,8 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         rb[set][2] = *(const u32x4*)(b1 + k0);
         rb[set][3] = *(const u32x4*)(b1 + k0 + 16);
     };
-    // Scales of quantized weights: a row's chunk of 512 k has 16 scale bytes (32 at 32-row
-    // tiles' 256-k chunks, 8).  E4M3: byte 4j + g scales lane group g in step j; E2M1: bytes
+    // Scales of quantized weights: a row's chunk of 512 k has 16 scale bytes (8 and 4 for the
+    // 256-k and 128-k chunks of larger tiles).  E4M3: byte 4j + g scales lane group g in step j; E2M1: bytes
     // 8j + 2g and 8j + 2g + 1.  The wave's two blocks' scale rows sit in its LDS area (row r
     // of block b at b*16*K/32 + r*K/32); sc holds the lane's row's bytes of the current chunk.
     constexpr int SCB = SKC / 32;                       // scale bytes per row and chunk
@@ -333,9 +335,11 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
                 if constexpr (SCB == 16) {
                     const u32x4 v = *(const u32x4*)p;
                     sc[b][0] = v[0], sc[b][1] = v[1], sc[b][2] = v[2], sc[b][3] = v[3];
-                } else {
+                } else if constexpr (SCB == 8) {
                     const uint2 v = *(const uint2*)p;
                     sc[b][0] = v.x, sc[b][1] = v.y;
+                } else {
+                    sc[b][0] = *(const uint32_t*)p;
                 }
             }
         }
@@ -437,8 +441,10 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     f32x4 acc[NRB][2];
 #pragma unroll
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NRB <= 2) {
-        constexpr int CHUNK = NRB <= 1 ? SKC : SKC2;   // the streaming loop's activation chunk
+    // the streaming loop takes tiles of up to 64 rows (E2M1: 32, its 256-k steps need chunks
+    // of at least 256 columns)
+    constexpr int CHUNK = stream_chunk(NRB);
+    if constexpr (NRB <= 4 && CHUNK >= 1024 / wbits(WF)) {
         if (c.K % CHUNK == 0 && (WF == WF_BF16 || c.K <= SCALE_KMAX))
             // E2M1 (16 MFMAs per block and step): weights one step ahead (two steps ahead
             // measured no faster; three spill)
@@ -931,13 +937,17 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 // the decode kernel (4-wave work-groups, two per CU) is 1-2% faster; above it the line
 // kernel wins, by 25% at 32-48 rows per expert (measured over 16..8192 tokens of the Beam
 // layer).  Quantized weights: the line kernel reads them in half or quarter lines, and the
-// decode kernel stays ahead up to 20 rows per expert (by 33-55% at 8, 9-23% at 20); the line
-// kernel wins from 24.
+// decode kernel's whole-line stream stays ahead longer: E4M3 (streaming tiles of up to 64
+// rows) up to 32 rows per expert (by 25% at 24, 13% at 32; the line kernel wins at 48), E2M1
+// (streaming tiles of up to 32 rows) up to 20.
 #ifndef WIDE_MIN_ROWS_PER_EXPERT
 #define WIDE_MIN_ROWS_PER_EXPERT 8
 #endif
-#ifndef WIDE_MIN_ROWS_PER_EXPERT_QUANT
-#define WIDE_MIN_ROWS_PER_EXPERT_QUANT 24
+#ifndef WIDE_MIN_ROWS_PER_EXPERT_E4M3
+#define WIDE_MIN_ROWS_PER_EXPERT_E4M3 40
+#endif
+#ifndef WIDE_MIN_ROWS_PER_EXPERT_E2M1
+#define WIDE_MIN_ROWS_PER_EXPERT_E2M1 24
 #endif
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4
@@ -948,7 +958,9 @@ static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, 
                         const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, const int32_t* sorted_pairs,
                         const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C,
                         hipStream_t s) {
-    constexpr int wide_min = WF == WF_BF16 ? WIDE_MIN_ROWS_PER_EXPERT : WIDE_MIN_ROWS_PER_EXPERT_QUANT;
+    constexpr int wide_min = WF == WF_BF16   ? WIDE_MIN_ROWS_PER_EXPERT
+                             : WF == WF_E4M3 ? WIDE_MIN_ROWS_PER_EXPERT_E4M3
+                                             : WIDE_MIN_ROWS_PER_EXPERT_E2M1;
     if (P >= (int64_t)wide_min * E && K % (2 * WKS) == 0) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;

@@ -175,6 +175,9 @@ MID_CASES = {
     # switch (24), so the decode kernel with tiles of every size
     "mid_fp8_serve_t160": mid_config("mid_fp8_serve_t160", 160, weights="fp8", seed_base=35000),
     "mid_mxfp4_serve_t160": mid_config("mid_mxfp4_serve_t160", 160, weights="mxfp4", seed_base=36000),
+    # 8-bit weights at 32 rows per expert (below their switch at 40): the stream's 64-row
+    # tiles (128-column chunks, 4 scale bytes per row and chunk)
+    "mid_fp8_serve_t256": mid_config("mid_fp8_serve_t256", 256, weights="fp8", seed_base=37000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
 }
