@@ -237,6 +237,11 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
 constexpr int SKC = 512;            // activation columns per LDS chunk (tiles of 16 rows)
 // activation columns per chunk for tiles of NRB row blocks: the same LDS bytes at every size
 __host__ __device__ constexpr int stream_chunk(int nrb) { return nrb <= 1 ? 512 : nrb <= 2 ? 256 : 128; }
+// bytes of each weight row per step: one 128-byte line; E2M1 at 64-row tiles half a line (a
+// whole line is 256 k, more than their 128-column chunks)
+__host__ __device__ constexpr int stream_step_bytes(int wf, int nrb) {
+    return wf == WF_E2M1 && stream_chunk(nrb) < 256 ? 64 : 128;
+}
 constexpr int SACT_ELEMS = 2 * 16 * SKC;   // the double-buffered activation chunks
 constexpr int SCALE_KMAX = 8192;    // longest K whose scale rows fit the per-wave LDS area
 constexpr int SCALE_WAVE_BYTES = 2 * 16 * (SCALE_KMAX / 32);
@@ -256,7 +261,8 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     static_assert(AL * THREADS == ACH, "activation chunk split");
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     constexpr int WB = wbits(WF);
-    constexpr int SW = 1024 / WB;                // k per step: one 128-byte line per row
+    constexpr int SB = stream_step_bytes(WF, NRB);  // bytes of each weight row per step
+    constexpr int SW = SB * 8 / WB;              // k per step
     constexpr int SKS_ = SKC / SW;               // steps per activation chunk
     static_assert(SKS_ >= 1, "a chunk holds at least one step");
     constexpr int U = RING / gcd_c(SKS_, RING);  // chunks per unrolled body: ring slots are static
@@ -282,17 +288,20 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 #pragma unroll
         for (int i = 0; i < AL; ++i) *(u32x4*)(lds + buf * (ROWS * SKC) + alds[i]) = sa[i];
     };
-    // weights: the 32 bytes at 32*g of the row's line hold the step's elements 16g .. +15
-    // (bf16), 32g .. +31 (E4M3: one 32-element scale block) or 64g .. +63 (E2M1: two blocks)
-    const uint8_t* b0 = c.bp0 + (lane >> 4) * (32 - WB);   // bp0 points at element 8g
-    const uint8_t* b1 = c.bp1 + (lane >> 4) * (32 - WB);
+    // weights: the SB/4 bytes at g*SB/4 of the row's step hold the lane's elements of the
+    // step: 16g .. +15 (bf16), 32g .. +31 (E4M3, and E2M1 in half-line steps: one 32-element
+    // scale block) or 64g .. +63 (E2M1 in whole-line steps: two blocks); one 16-byte load per
+    // 16 bytes
+    constexpr int LB = SB / 64;                  // 16-byte loads per block and step
+    const uint8_t* b0 = c.bp0 + (lane >> 4) * (SB / 4 - WB);   // bp0 points at element 8g
+    const uint8_t* b1 = c.bp1 + (lane >> 4) * (SB / 4 - WB);
     u32x4 rb[RING][4];
     auto load_b = [&](int kstep, int set) {
-        const int k0 = (kstep < nk ? kstep : nk - 1) * 128;
-        rb[set][0] = *(const u32x4*)(b0 + k0);
-        rb[set][1] = *(const u32x4*)(b0 + k0 + 16);
-        rb[set][2] = *(const u32x4*)(b1 + k0);
-        rb[set][3] = *(const u32x4*)(b1 + k0 + 16);
+        const int k0 = (kstep < nk ? kstep : nk - 1) * SB;
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[set][i] = *(const u32x4*)(b0 + k0 + 16 * i);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[set][2 + i] = *(const u32x4*)(b1 + k0 + 16 * i);
     };
     // Scales of quantized weights: a row's chunk of 512 k has 16 scale bytes (8 and 4 for the
     // 256-k and 128-k chunks of larger tiles).  E4M3: byte 4j + g scales lane group g in step j; E2M1: bytes
@@ -346,9 +355,9 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     };
     // scale of block h (0, 1) of the lane's elements in step j of the chunk
     auto scale_of = [&](int blk, int j, int h) {
-        if constexpr (WF == WF_E4M3) {
+        if constexpr (SW == 128) {   // one block per lane and step: byte 4j + g
             return e8m0_factor((sc[blk][j] >> (8 * (lane >> 4))) & 0xFFu);
-        } else {
+        } else {                     // two: bytes 8j + 2g + h
             const uint32_t d = (lane & 32) ? sc[blk][2 * j + 1] : sc[blk][2 * j];
             return e8m0_factor((d >> (8 * (2 * ((lane >> 4) & 1) + h))) & 0xFFu);
         }
@@ -360,7 +369,7 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         float s0[2] = {0.f, 0.f}, s1[2] = {0.f, 0.f};
         if constexpr (WF != WF_BF16) {
 #pragma unroll
-            for (int h = 0; h < (WF == WF_E2M1 ? 2 : 1); ++h) {
+            for (int h = 0; h < SW / 128; ++h) {
                 s0[h] = scale_of(0, j, h);
                 s1[h] = scale_of(1, j, h);
             }
@@ -441,14 +450,14 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     f32x4 acc[NRB][2];
 #pragma unroll
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the streaming loop takes tiles of up to 64 rows (E2M1: 32, its 256-k steps need chunks
-    // of at least 256 columns)
+    // the streaming loop takes tiles of up to 64 rows
     constexpr int CHUNK = stream_chunk(NRB);
-    if constexpr (NRB <= 4 && CHUNK >= 1024 / wbits(WF)) {
+    if constexpr (NRB <= 4) {
         if (c.K % CHUNK == 0 && (WF == WF_BF16 || c.K <= SCALE_KMAX))
-            // E2M1 (16 MFMAs per block and step): weights one step ahead (two steps ahead
-            // measured no faster; three spill)
-            tile_body_stream<GATED, WF, NRB, WF == WF_E2M1 ? 2 : RING, THREADS>(c, &lds[0][0], acc);
+            // E2M1 in whole-line steps (16 MFMAs per block and step): weights one step ahead
+            // (two steps ahead measured no faster; three spill)
+            tile_body_stream<GATED, WF, NRB, stream_step_bytes(WF, NRB) * 8 / wbits(WF) == 256 ? 2 : RING,
+                             THREADS>(c, &lds[0][0], acc);
         else
             tile_body<GATED, WF, NRB, RING, THREADS>(c, lds, acc);
     } else
@@ -937,9 +946,9 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 // the decode kernel (4-wave work-groups, two per CU) is 1-2% faster; above it the line
 // kernel wins, by 25% at 32-48 rows per expert (measured over 16..8192 tokens of the Beam
 // layer).  Quantized weights: the line kernel reads them in half or quarter lines, and the
-// decode kernel's whole-line stream stays ahead longer: E4M3 (streaming tiles of up to 64
-// rows) up to 32 rows per expert (by 25% at 24, 13% at 32; the line kernel wins at 48), E2M1
-// (streaming tiles of up to 32 rows) up to 20.
+// decode kernel's stream (tiles of up to 64 rows) stays ahead longer: E4M3 up to 36 rows
+// per expert (by 25% at 24, 13% at 32; even at 40, the line kernel ahead at 44), E2M1 up to
+// 40 (by 42% at 24, 11% at 40; the line kernel ahead at 48).
 #ifndef WIDE_MIN_ROWS_PER_EXPERT
 #define WIDE_MIN_ROWS_PER_EXPERT 8
 #endif
@@ -947,7 +956,7 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 #define WIDE_MIN_ROWS_PER_EXPERT_E4M3 40
 #endif
 #ifndef WIDE_MIN_ROWS_PER_EXPERT_E2M1
-#define WIDE_MIN_ROWS_PER_EXPERT_E2M1 24
+#define WIDE_MIN_ROWS_PER_EXPERT_E2M1 44
 #endif
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4
