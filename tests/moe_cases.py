@@ -178,6 +178,8 @@ MID_CASES = {
     # 8-bit weights at 32 rows per expert (below their switch at 40): the stream's 64-row
     # tiles (128-column chunks, 4 scale bytes per row and chunk)
     "mid_fp8_serve_t256": mid_config("mid_fp8_serve_t256", 256, weights="fp8", seed_base=37000),
+    # ... and 4-bit weights there (below their switch at 44): the 64-row tiles' half-line steps
+    "mid_mxfp4_serve_t256": mid_config("mid_mxfp4_serve_t256", 256, weights="mxfp4", seed_base=39000),
     # 256 experts at 6 rows per expert, skewed: tiles of up to 200 rows on the decode kernel
     # (its 32-k loop for tiles above 64 rows, the stream below), in all three formats
     "mid_skew_e256_t200": mid_config("mid_skew_e256_t200", 200, E=256, bias="zipf:0.6", seed_base=38000),
