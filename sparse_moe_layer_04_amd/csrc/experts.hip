@@ -8,12 +8,12 @@
 //   down:     y_pair[p, :] = h[r, :] W_d[e]^T
 // where row r of the expert-sorted pair list holds pair p = t*top_k + j routed to e.
 //
-// bf16 path (details below): one work-group computes one (tile, column block) on
-// bf16 MFMA.  Expert weights are bf16, or E4M3 / E2M1 codes with E8M0 block scales that
-// are decoded exactly to bf16 in registers (template parameter WF).  Gate/up column blocks hold the gate and the up rows of the same output
-// columns, so the SwiGLU epilogue has both operands in registers.  The gate/up A
-// operand is gathered straight from the token rows (no permuted copy); the down
-// epilogue scatters each row to its pair position.
+// bf16 path (details below): one work-group computes one (tile, column block) on bf16
+// MFMA.  Expert weights are bf16, or E4M3 / E2M1 codes with E8M0 block scales that are
+// decoded exactly to bf16 in registers (template parameter WF).  Gate/up column blocks
+// hold the gate and the up rows of the same output columns, so the SwiGLU epilogue has
+// both operands in registers.  The gate/up A operand is gathered straight from the token
+// rows (no permuted copy); the down epilogue scatters each row to its pair position.
 #include "common.hpp"
 
 #include <type_traits>
@@ -34,9 +34,7 @@ namespace beam {
 // both streams, so they share the prefetch distance).
 // ---------------------------------------------------------------------------------
 constexpr int GROWS = 288;    // rows per tile: at 8192 tokens almost every expert fits one tile
-constexpr int GRB = GROWS / 16;
 constexpr int GKS = 32;       // k per step (one MFMA)
-constexpr int GRING = 4;      // register sets: 3 steps in flight + 1 in use
 
 // LDS element offset of 16-byte chunk `ch` (0..3) of activation row `row` (64-byte rows).
 // The MFMA operand read (lane -> row lane&15, chunk lane>>4) and the staging write are
@@ -101,7 +99,7 @@ __device__ __forceinline__ const uint16_t* act_row(const TileCtx& c, int row) {
     return c.A + r * c.K;
 }
 
-// Main loop for tiles of at most NRB 16-row blocks (the decode-sized NRB <= 2 take the
+// Main loop for tiles of at most NRB 16-row blocks (tiles of up to 4 blocks take the
 // streaming loop below when K is a multiple of its chunk).  Activations go
 // through an LDS double buffer: one register set stages step kt+2 while step kt+1 is
 // written to LDS and step kt is multiplied; weights stream RING-1 steps ahead.  Within
@@ -223,12 +221,13 @@ __device__ __forceinline__ void tile_body(const TileCtx& c, uint16_t (*lds)[GROW
     }
 }
 
-// Main loop for tiles of at most NRB <= 2 row blocks (decode-sized), where the weight
+// Main loop for tiles of at most NRB <= 4 row blocks (decode-sized), where the weight
 // stream is the whole cost.  A step covers one 128-byte line of every weight row (64 k of
-// bf16, 128 k of E4M3, 256 k of E2M1): lane (row, g = lane>>4) of a 16-row block loads
-// the 32 bytes at 32*g of its row's line with two 16-byte loads, so every load
-// instruction covers whole lines of 16 rows; the step's MFMAs take the lane's elements 8
-// at a time (the activation operand uses the same k order).  Weights run RING-1 steps
+// bf16, 128 k of E4M3, 256 k of E2M1; E2M1 at 64-row tiles half a line, 128 k): lane
+// (row, g = lane>>4) of a 16-row block loads the 32 bytes at 32*g of its row's line with
+// two 16-byte loads (half lines: the 16 bytes at 16*g), so the loads of a step cover whole
+// lines of 16 rows; the step's MFMAs take the lane's elements 8 at a time (the activation
+// operand uses the same k order).  Weights run RING-1 steps
 // ahead.  Activations are staged through LDS in chunks of SKC columns for all rows of the
 // tile (one barrier per chunk); the next chunk's global loads are issued a whole chunk
 // ahead.  Quantized weights: each wave copies the scale rows of its two blocks (16 rows x
@@ -551,7 +550,7 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
     c.top_k = top_k;
     c.gather = GATED;
 
-    // row-count variants; small tiles are load-latency bound and keep 7 steps in flight
+    // row-count variants (tiles of up to 4 row blocks stream; larger ones take 32-k steps)
     const int nrb = (te.row_count + 15) >> 4;
 
     constexpr int TH = WAVES * 64;
