@@ -100,7 +100,7 @@ def load_traffic(workload, kernel):
         return None
 
 
-# expert GEMM kernels (the 8-wave decode kernel or the line-streaming prefill kernel) by template flag
+# expert GEMM kernels (the decode kernel or the line-streaming kernel) by their GATED template flag
 KERNEL_NAMES = {"gate_up": "<true", "down": "<false"}
 
 
