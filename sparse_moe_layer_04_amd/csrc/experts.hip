@@ -934,6 +934,11 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
 constexpr int LINE_WAVES = 8;
 constexpr int LINE_NB = 2;
 constexpr int LINE_RING = 2;
+// E2M1 weights (8 bytes per block and step) two steps ahead: 4-6% faster from 48 rows per
+// expert through prefill; E4M3 spills with a third register set
+#ifndef LINE_RING_Q
+#define LINE_RING_Q 3
+#endif
 
 int gemm_tile_rows(int64_t P, int E, bool bf16) {
     (void)P;
@@ -972,7 +977,7 @@ static void launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, 
     if (P >= (int64_t)wide_min * E && K % (2 * WKS) == 0) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-        moe_gemm_line_kernel<GATED, WF, LINE_WAVES, LINE_NB, LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
+        moe_gemm_line_kernel<GATED, WF, LINE_WAVES, LINE_NB, WF == WF_E2M1 ? LINE_RING_Q : LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
             A, (uint32_t)a_bytes, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
     } else {
         // decode-sized: 4-wave work-groups (two per compute unit) over half-width column
