@@ -22,16 +22,8 @@ namespace beam {
 // different work-groups (small T needs the parallelism); each writes an fp64 partial
 // and the selection kernel adds the partials in split order before rounding the logit
 // once to fp32, so the result does not depend on scheduling.
-//
-// Work-group: 4 waves, 64 tokens x 128 experts; wave w owns experts [32w, 32w+32) of
-// all 64 tokens, so each split of a router weight feeds 4 row blocks.  Operands are
-// read straight from global memory (the matrix is cache-resident), with the loads of
-// the next step in flight.
 // ---------------------------------------------------------------------------------
-constexpr int RL_TOK = 64;           // tokens per work-group
-constexpr int RL_RB = RL_TOK / 16;   // 16-row MFMA blocks per wave
-constexpr int RL_EXP = 128;          // experts per work-group (32 per wave)
-constexpr int RL_RING = 2;           // register sets: the next step's loads are in flight
+constexpr int RL_KUNIT = 64;   // split granularity: klen is a multiple of 64 columns
 
 __device__ __forceinline__ void split3(float w, float& hi, float& mid, float& lo) {
     hi = __uint_as_float(__float_as_uint(w) & 0xFFFF0000u);
@@ -46,63 +38,94 @@ __device__ __forceinline__ __bf16 as_bf16_trunc(float f) {
 }
 
 // x [T,H] bf16, wr [E,H] fp32 -> part [nsplit][T][E] fp64 (split s covers columns
-// [s*klen, (s+1)*klen), klen a multiple of 32 * RL_RING).
+// [s*klen, (s+1)*klen), klen a multiple of 32).
+//
+// A work-group of 4 waves covers TOK = 16*RB tokens x 64*CB experts (RB*CB = 8): wave w
+// owns CB 16-expert blocks of all RB token blocks, so each split weight feeds RB MFMAs.
+// Each 32-k step is staged through LDS: the four lanes of every quad load 64 contiguous
+// bytes of one row of x or W_r.  Loaded straight in the MFMA layout, each quad would
+// touch four rows and the L1 would process the loads at a quarter of its rate; x would
+// also be fetched by all four waves.  Fragments are read back with an XOR swizzle on
+// the 16-byte piece index, so the lanes of every ds_read_b128 / ds_write_b128 phase hit
+// distinct banks (for phases of 8 lanes over 128 bytes and of 16 lanes over 256).
+__device__ __forceinline__ int rl_x_off(int row, int piece) {   // 4 pieces of 16 B per row
+    return row * 64 + ((piece ^ ((row >> 1) & 3) ^ ((row >> 3) & 1)) << 4);
+}
+__device__ __forceinline__ int rl_w_off(int row, int piece) {   // 8 pieces of 16 B per row
+    return row * 128 + ((piece ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
+
+template <int RB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) router_logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr, int64_t T, int H,
                                                                  int E, int klen, double* __restrict__ part) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * RL_TOK;
-    const int e0 = blockIdx.y * RL_EXP + wave * 32;
+    constexpr int CB = 8 / RB, TOK = 16 * RB, EXP = 64 * CB;
+    constexpr int XS = TOK * 64, BUF = XS + EXP * 128;   // bytes of x, then W_r, per step
+    constexpr int XP = TOK / 64, WP = 2 * CB;             // 16-byte pieces per thread
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * TOK;
+    const int eb = blockIdx.y * EXP;
     const int split = blockIdx.z;
-    if (e0 >= E) return;  // whole wave idle (uniform)
 
-    const int kq = (lane >> 4) * 8 + split * klen;  // k offset of this lane
-    const uint16_t* arow[RL_RB];
-    const float* brow[2];
-    for (int rb = 0; rb < RL_RB; ++rb) {
-        const int64_t t = t0 + rb * 16 + (lane & 15);
-        arow[rb] = x + (t < T ? t : T - 1) * (int64_t)H + kq;  // rows past T repeat row T-1
+    // global sources of this thread's pieces (rows past T or E repeat the last row)
+    const uint16_t* xsrc[XP];
+    int xoff[XP], woff[WP];
+    const float* wsrc[WP];
+    for (int i = 0; i < XP; ++i) {
+        const int n = i * 256 + tid, r = n >> 2;
+        const int64_t t = t0 + r < T ? t0 + r : T - 1;
+        xsrc[i] = x + t * (int64_t)H + split * klen + (n & 3) * 8;
+        xoff[i] = rl_x_off(r, n & 3);
     }
-    for (int cb = 0; cb < 2; ++cb) {
-        const int e = e0 + cb * 16 + (lane & 15);
-        brow[cb] = wr + (int64_t)(e < E ? e : E - 1) * H + kq;
+    for (int i = 0; i < WP; ++i) {
+        const int n = i * 256 + tid, r = n >> 3;
+        const int e = eb + r < E ? eb + r : E - 1;
+        wsrc[i] = wr + (int64_t)e * H + split * klen + (n & 7) * 4;
+        woff[i] = XS + rl_w_off(r, n & 7);
     }
+    u32x4 gx[XP];
+    f32x4 gw[WP];
+    auto gload = [&](int ks) {
+        for (int i = 0; i < XP; ++i) gx[i] = *(const u32x4*)(xsrc[i] + ks * 32);
+        for (int i = 0; i < WP; ++i) gw[i] = *(const f32x4*)(wsrc[i] + ks * 32);
+    };
+    auto lstore = [&](int buf) {
+        unsigned char* b = lds + buf * BUF;
+        for (int i = 0; i < XP; ++i) *(u32x4*)(b + xoff[i]) = gx[i];
+        for (int i = 0; i < WP; ++i) *(f32x4*)(b + woff[i]) = gw[i];
+    };
 
-    f32x4 acc[RL_RB][2];
-    double acc64[RL_RB][2][4];
-    for (int i = 0; i < RL_RB; ++i)
-        for (int j = 0; j < 2; ++j)
+    f32x4 acc[RB][CB];
+    double acc64[RB][CB][4];
+    for (int i = 0; i < RB; ++i)
+        for (int j = 0; j < CB; ++j)
             for (int q = 0; q < 4; ++q) acc64[i][j][q] = 0.0;
 
-    u32x4 ra[RL_RING][RL_RB];
-    f32x4 rw[RL_RING][2][2];
-    const int nks = klen / 32;
-    auto load = [&](int ks, int set) {
-        const int k0 = (ks < nks ? ks : nks - 1) * 32;
-        for (int rb = 0; rb < RL_RB; ++rb) ra[set][rb] = *(const u32x4*)(arow[rb] + k0);
-        for (int cb = 0; cb < 2; ++cb) {
-            rw[set][cb][0] = *(const f32x4*)(brow[cb] + k0);
-            rw[set][cb][1] = *(const f32x4*)(brow[cb] + k0 + 4);
-        }
-    };
-    auto step = [&](int ks, int set) {
-        load(ks + RL_RING - 1, (set + RL_RING - 1) % RL_RING);
-        for (int i = 0; i < RL_RB; ++i)
-            for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 a[RL_RB];
-        for (int rb = 0; rb < RL_RB; ++rb) a[rb] = __builtin_bit_cast(bf16x8, ra[set][rb]);
-        for (int cb = 0; cb < 2; ++cb) {
+    const int kg = lane >> 4;   // this lane's 8-k group of the 32-k step
+    auto compute = [&](int buf) {
+        const unsigned char* b = lds + buf * BUF;
+        bf16x8 a[RB];
+        for (int rb = 0; rb < RB; ++rb)
+            a[rb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(b + rl_x_off(rb * 16 + (lane & 15), kg)));
+        for (int i = 0; i < RB; ++i)
+            for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < CB; ++cb) {
+            const int row = (wave * CB + cb) * 16 + (lane & 15);
+            const f32x4 w0 = *(const f32x4*)(b + XS + rl_w_off(row, 2 * kg));
+            const f32x4 w1 = *(const f32x4*)(b + XS + rl_w_off(row, 2 * kg + 1));
             bf16x8 bh, bm, bl;
             for (int q = 0; q < 8; ++q) {
-                const float w = q < 4 ? rw[set][cb][0][q] : rw[set][cb][1][q - 4];
+                const float w = q < 4 ? w0[q] : w1[q - 4];
                 float hi, mid, lo;
                 split3(w, hi, mid, lo);
                 bh[q] = as_bf16_trunc(hi);
                 bm[q] = as_bf16_trunc(mid);
                 bl[q] = as_bf16_trunc(lo);
             }
-            for (int rb = 0; rb < RL_RB; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bl, acc[rb][cb], 0, 0, 0);
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bm, acc[rb][cb], 0, 0, 0);
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bh, acc[rb][cb], 0, 0, 0);
@@ -110,21 +133,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) r
         }
         // fold each 32-term block into fp64: the matrix-core sum rounds once per
         // instruction, so short fp32 chains keep the logit error near one fp32 ulp
-        for (int i = 0; i < RL_RB; ++i)
-            for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < RB; ++i)
+            for (int j = 0; j < CB; ++j)
                 for (int q = 0; q < 4; ++q) acc64[i][j][q] += (double)acc[i][j][q];
     };
-    for (int s = 0; s < RL_RING - 1; ++s) load(s, s);
-    static_assert(4 % RL_RING == 0, "nks is a multiple of 4");
-    for (int ks = 0; ks < nks; ks += RL_RING) {
-#pragma unroll
-        for (int j = 0; j < RL_RING; ++j) step(ks + j, j);
+
+    const int nks = klen / 32;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+        const bool more = ks + 1 < nks;
+        if (more) gload(ks + 1);   // in flight while this step's MFMAs run
+        compute(ks & 1);
+        if (more) lstore((ks + 1) & 1);
+        __syncthreads();
     }
     // C layout of a 16x16 MFMA block: lane holds rows 4*(lane>>4)+q, column lane&15
     double* out = part + (int64_t)split * T * E;
-    for (int rb = 0; rb < RL_RB; ++rb)
-        for (int cb = 0; cb < 2; ++cb) {
-            const int e = e0 + cb * 16 + (lane & 15);
+    for (int rb = 0; rb < RB; ++rb)
+        for (int cb = 0; cb < CB; ++cb) {
+            const int e = eb + (wave * CB + cb) * 16 + (lane & 15);
             for (int q = 0; q < 4; ++q) {
                 const int64_t t = t0 + rb * 16 + 4 * (lane >> 4) + q;
                 if (t < T && e < E) out[t * E + e] = acc64[rb][cb][q];
@@ -132,9 +161,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) r
         }
 }
 
+// 128-token tiles from 128 tokens on (half the weight splits per MFMA); smaller batches
+// keep 64-token tiles so that fewer MFMA row blocks are padding.
+constexpr int64_t RL_WIDE_MIN_T = 128;
+static int router_rb(int64_t T) { return T >= RL_WIDE_MIN_T ? 8 : 4; }
+
 int router_splits(int64_t T, int H, int E) {
-    const int64_t tiles = ((T + RL_TOK - 1) / RL_TOK) * ((E + RL_EXP - 1) / RL_EXP);
-    const int units = H / (32 * RL_RING);  // split granularity
+    const int rb = router_rb(T), tok = 16 * rb, exp = 512 / rb;
+    const int64_t tiles = ((T + tok - 1) / tok) * ((E + exp - 1) / exp);
+    const int units = H / RL_KUNIT;
     int best = 1;
     for (int d = 1; d <= units; ++d)
         if (units % d == 0 && tiles * d <= 1024) best = d;
@@ -158,8 +193,12 @@ hipError_t launch_router_logits(const void* x, bool bf16, const float* w_router,
                                 int nsplit, double* part, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (bf16) {
-        dim3 grid((unsigned)((T + RL_TOK - 1) / RL_TOK), (unsigned)((E + RL_EXP - 1) / RL_EXP), (unsigned)nsplit);
-        router_logits_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, w_router, T, H, E, H / nsplit, part);
+        const int rb = router_rb(T), tok = 16 * rb, exp = 512 / rb;
+        dim3 grid((unsigned)((T + tok - 1) / tok), (unsigned)((E + exp - 1) / exp), (unsigned)nsplit);
+        if (rb == 8)
+            router_logits_bf16_kernel<8><<<grid, 256, 0, s>>>((const uint16_t*)x, w_router, T, H, E, H / nsplit, part);
+        else
+            router_logits_bf16_kernel<4><<<grid, 256, 0, s>>>((const uint16_t*)x, w_router, T, H, E, H / nsplit, part);
     } else {
         int64_t n = T * E;
         unsigned blocks = (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
@@ -289,8 +328,11 @@ __global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double
     if (tt >= ntok) return;
     const int64_t t = tb + tt;
 
-    // lane owns experts lane, lane+64, ...; `taken` marks its chosen ones
-    uint32_t taken = 0;
+    // lane owns experts lane, lane+64, ...; `avail` marks those still available (in a
+    // kept group, not yet chosen)
+    uint32_t avail = 0;
+    for (int q = 0, e = lane; e < E; ++q, e += 64)
+        if (s_kept[tt][e / gsize]) avail |= 1u << q;
     float ssum = 0.f;
     int my_e = -1;
     float my_s = 0.f;
@@ -298,7 +340,7 @@ __global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double
         float bv = -INFINITY;
         int bi = 0x7fffffff;
         for (int q = 0, e = lane; e < E; ++q, e += 64) {
-            if (((taken >> q) & 1u) || !s_kept[tt][e / gsize]) continue;
+            if (!((avail >> q) & 1u)) continue;
             const float v = s_sb[tt][e];
             if (ranks_before(v, e, bv, bi)) {
                 bv = v;
@@ -315,7 +357,7 @@ __global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double
         }
         // non-finite scores compare false everywhere; keep the index in range regardless
         if (bi < 0 || bi >= E) bi = 0;
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
         const float sc = s_sc[tt][bi];
         ssum += sc;
         if (lane == j) {
