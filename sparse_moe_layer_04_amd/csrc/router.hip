@@ -224,6 +224,18 @@ __device__ __forceinline__ bool ranks_before(float va, int a, float vb, int b) {
     return va > vb || (va == vb && a < b);
 }
 
+// one exchange of a (score, index) argmax between lanes paired by a DPP pattern that
+// stays inside each row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ void sel_dpp_step(float& bv, int& bi) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+    if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
 __global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double* __restrict__ part, int nsplit,
                                                                     const float* __restrict__ bias, int64_t T, int E,
                                                                     int n_group, int topk_group, int top_k,
@@ -301,19 +313,31 @@ __global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double
         }
     }
     __syncthreads();
-    for (int i = tid; i < ntok * n_group; i += SEL_THREADS) {
-        const int tt = i / n_group, g = i - tt * n_group;
+    // group scores: the wave of token tt gives each group L lanes (L a power of two, L *
+    // n_group <= 64); each lane keeps the two largest biased scores of its slice, and the
+    // L lanes merge their pairs (the top two of four values) by butterfly exchange
+    {
+        const int tt = tid >> 6;
+        int lg = 0;
+        while ((2 << lg) * n_group <= 64) ++lg;
+        const int L = 1 << lg, g = lane >> lg, sub = lane & (L - 1);
         float a1 = -INFINITY, a2 = -INFINITY;
-        for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
-            const float v = s_sb[tt][e];
-            if (v > a1) {
-                a2 = a1;
-                a1 = v;
-            } else if (v > a2) {
-                a2 = v;
+        if (tt < ntok && g < n_group)
+            for (int e = g * gsize + sub; e < (g + 1) * gsize; e += L) {
+                const float v = s_sb[tt][e];
+                if (v > a1) {
+                    a2 = a1;
+                    a1 = v;
+                } else if (v > a2) {
+                    a2 = v;
+                }
             }
+        for (int off = 1; off < L; off <<= 1) {
+            const float b1 = __shfl_xor(a1, off), b2 = __shfl_xor(a2, off);
+            a2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+            a1 = fmaxf(a1, b1);
         }
-        s_gs[tt][g] = gsize >= 2 ? a1 + a2 : a1;
+        if (tt < ntok && g < n_group && sub == 0) s_gs[tt][g] = gsize >= 2 ? a1 + a2 : a1;
     }
     __syncthreads();
     for (int i = tid; i < ntok * n_group; i += SEL_THREADS) {
@@ -347,13 +371,24 @@ __global__ void __launch_bounds__(SEL_THREADS) router_select_kernel(const double
                 bi = e;
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ranks_before(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
+        // best of each row of 16 lanes (DPP exchanges), then of the four rows
+        sel_dpp_step<0xB1>(bv, bi);    // quad_perm [1,0,3,2]
+        sel_dpp_step<0x4E>(bv, bi);    // quad_perm [2,3,0,1]
+        sel_dpp_step<0x141>(bv, bi);   // row_half_mirror
+        sel_dpp_step<0x140>(bv, bi);   // row_mirror
+        {
+            float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+            int gi = __builtin_amdgcn_readlane(bi, 0);
+            for (int r = 16; r < 64; r += 16) {
+                const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r));
+                const int oi = __builtin_amdgcn_readlane(bi, r);
+                if (ranks_before(ov, oi, gv, gi)) {
+                    gv = ov;
+                    gi = oi;
+                }
             }
+            bv = gv;
+            bi = gi;
         }
         // non-finite scores compare false everywhere; keep the index in range regardless
         if (bi < 0 || bi >= E) bi = 0;
