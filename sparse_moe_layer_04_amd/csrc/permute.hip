@@ -5,7 +5,8 @@
 // (2) one work-group scans the counts per expert over chunks and over experts, giving
 // every chunk a base row per expert, the expert offsets and the tile list; (3) one
 // wave per chunk walks its pairs in order and ranks equal experts with ballots, so
-// rows inside an expert stay in ascending pair order (deterministic output).
+// rows inside an expert stay in ascending pair order (deterministic output).  A single
+// chunk runs the three steps in one work-group.
 #include "common.hpp"
 
 namespace beam {
@@ -34,17 +35,19 @@ __global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One work-group of 1024 threads.  Thread t handles expert t % E for chunk group
-// t / E (G = 1024 / E groups of consecutive chunks), so the per-expert scan over
-// chunks runs in G pieces with coalesced reads of the count rows.
-__global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ counts, int nchunks, int E, int64_t P,
-                                                         int32_t* __restrict__ offsets, TileEntry* __restrict__ tiles,
-                                                         int32_t* __restrict__ num_tiles, int tile_rows) {
+// Scan by one work-group of 1024 threads.  Thread t handles expert t % E for chunk
+// group t / E (G = 1024 / E groups of consecutive chunks), so the per-expert scan over
+// chunks runs in G pieces with coalesced reads of the count rows; the scans over experts
+// are prefix sums across the work-group.
+__device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int nchunks, int E,
+                                               int32_t* __restrict__ offsets, TileEntry* __restrict__ tiles,
+                                               int32_t* __restrict__ num_tiles, int tile_rows) {
     __shared__ int32_t part[1024];  // [group][expert] chunk-range sums, then group bases
     __shared__ int32_t tot[PERM_MAX_E];
     __shared__ int32_t off[PERM_MAX_E];
     __shared__ int32_t ntl[PERM_MAX_E];
     __shared__ int32_t toff[PERM_MAX_E];
+    __shared__ int32_t wsum[2][16];
     const int tid = threadIdx.x;
     const int G = 1024 / E;  // >= 1 since E <= 1024
     const int e = tid % E, g = tid / E;
@@ -69,17 +72,36 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ c
         ntl[tid] = run > 0 ? (run + tile_rows - 1) / tile_rows : 0;
     }
     __syncthreads();
-    // (3) exclusive scans over experts (E <= 1024: a single pass by one thread is cheap)
-    if (tid == 0) {
-        int32_t a = 0, b = 0;
-        for (int k = 0; k < E; ++k) {
-            off[k] = a;
-            a += tot[k];
-            toff[k] = b;
-            b += ntl[k];
+    // (3) exclusive scans over experts of the row counts and the tile counts: inclusive
+    // scans inside each wave by shuffles, then the totals of the earlier waves
+    {
+        const int lane = tid & 63, w = tid >> 6;
+        int32_t a = tid < E ? tot[tid] : 0, b = tid < E ? ntl[tid] : 0;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t ua = __shfl_up(a, o), ub = __shfl_up(b, o);
+            if (lane >= o) {
+                a += ua;
+                b += ub;
+            }
         }
-        offsets[E] = a;
-        if (num_tiles) *num_tiles = b;
+        if (lane == 63) {
+            wsum[0][w] = a;
+            wsum[1][w] = b;
+        }
+        __syncthreads();
+        int32_t pa = 0, pb = 0;
+        for (int v = 0; v < w; ++v) {
+            pa += wsum[0][v];
+            pb += wsum[1][v];
+        }
+        if (tid < E) {
+            off[tid] = pa + a - tot[tid];
+            toff[tid] = pb + b - ntl[tid];
+        }
+        if (tid == 1023) {  // ids past E add zero
+            offsets[E] = pa + a;
+            if (num_tiles) *num_tiles = pb + b;
+        }
     }
     __syncthreads();
     // (4) every chunk's first row per expert: expert offset + earlier chunks' counts
@@ -112,6 +134,45 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ c
     }
 }
 
+__global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ counts, int nchunks, int E,
+                                                         int32_t* __restrict__ offsets, TileEntry* __restrict__ tiles,
+                                                         int32_t* __restrict__ num_tiles, int tile_rows) {
+    perm_scan_body(counts, nchunks, E, offsets, tiles, num_tiles, tile_rows);
+}
+
+// One wave places the 64 pairs [pb, pb + 64) of a chunk ending at p1: lanes with equal
+// experts are ranked by ballots in pair order, and `next` holds each expert's next row.
+// The caller makes the cursor updates visible (a barrier) before the next 64 pairs.
+__device__ __forceinline__ void perm_scatter_step(const int32_t* __restrict__ idx, int64_t pb, int64_t p1, int E,
+                                                  int ebits, int32_t* next, int32_t* __restrict__ sorted_pairs,
+                                                  int32_t* __restrict__ pair_pos, int lane) {
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t p = pb + lane;
+    int e = p < p1 ? idx[p] : -1;
+    const bool valid = e >= 0 && e < E;  // out-of-range ids are skipped
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    if (valid) {
+        const int rank = __popcll(peers & lt_mask);
+        const int32_t dest = next[e] + rank;
+        sorted_pairs[dest] = (int32_t)p;
+        pair_pos[p] = dest;
+        // the highest lane of the peer group advances the expert's cursor
+        if ((peers >> lane) == 1ull) next[e] += __popcll(peers);
+    }
+}
+
+__device__ __forceinline__ int perm_ebits(int E) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    return ebits;
+}
+
 __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
                                                           const int32_t* __restrict__ base,
                                                           int32_t* __restrict__ sorted_pairs,
@@ -120,30 +181,45 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
     const int lane = threadIdx.x;
     for (int e = lane; e < E; e += 64) next[e] = base[(int64_t)blockIdx.x * E + e];
     __syncthreads();
-    int ebits = 0;
-    while ((1 << ebits) < E) ++ebits;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int ebits = perm_ebits(E);
     const int64_t p0 = (int64_t)blockIdx.x * PERM_CHUNK;
     const int64_t p1 = p0 + PERM_CHUNK < P ? p0 + PERM_CHUNK : P;
     for (int64_t pb = p0; pb < p1; pb += 64) {
-        const int64_t p = pb + lane;
-        int e = p < p1 ? idx[p] : -1;
-        const bool valid = e >= 0 && e < E;  // out-of-range ids are skipped
-        if (!valid) e = 0;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < ebits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        if (valid) {
-            const int rank = __popcll(peers & lt_mask);
-            const int32_t dest = next[e] + rank;
-            sorted_pairs[dest] = (int32_t)p;
-            pair_pos[p] = dest;
-            // the highest lane of the peer group advances the expert's cursor
-            if ((peers >> lane) == 1ull) next[e] += __popcll(peers);
-        }
+        perm_scatter_step(idx, pb, p1, E, ebits, next, sorted_pairs, pair_pos, lane);
+        __syncthreads();
+    }
+}
+
+// All pairs in one chunk (1 <= P <= PERM_CHUNK): histogram, scan and scatter in one
+// work-group of 1024 threads, saving two dependent launches for decode-sized batches.
+// The histogram goes through `counts` (E words of the scratch) so the scan reads it as
+// in the multi-chunk path; wave 0 then places the pairs.
+__global__ void __launch_bounds__(1024) perm_single_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pairs,
+                                                           int32_t* __restrict__ pair_pos,
+                                                           TileEntry* __restrict__ tiles,
+                                                           int32_t* __restrict__ num_tiles, int tile_rows) {
+    __shared__ int32_t cnt[PERM_MAX_E];
+    __shared__ int32_t next[PERM_MAX_E];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    if (tid < P) {
+        const int e = idx[tid];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024) counts[e] = cnt[e];
+    __syncthreads();
+    perm_scan_body(counts, 1, E, offsets, tiles, num_tiles, tile_rows);
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024) next[e] = counts[e];
+    __syncthreads();
+    const int ebits = perm_ebits(E);
+    for (int64_t pb = 0; pb < P; pb += 64) {
+        if (tid < 64) perm_scatter_step(idx, pb, P, E, ebits, next, sorted_pairs, pair_pos, tid);
         __syncthreads();
     }
 }
@@ -152,8 +228,13 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* scratch
                           int32_t* sorted_pairs, int32_t* pair_pos, TileEntry* tiles, int32_t* num_tiles,
                           int tile_rows, hipStream_t s) {
     int nchunks = (int)((P + PERM_CHUNK - 1) / PERM_CHUNK);
+    if (nchunks == 1) {
+        perm_single_kernel<<<1, 1024, 0, s>>>(idx, P, E, scratch, offsets, sorted_pairs, pair_pos, tiles, num_tiles,
+                                              tile_rows);
+        return hipGetLastError();
+    }
     if (nchunks > 0) perm_hist_kernel<<<nchunks, 256, 0, s>>>(idx, P, E, scratch);
-    perm_scan_kernel<<<1, 1024, 0, s>>>(scratch, nchunks, E, P, offsets, tiles, num_tiles, tile_rows);
+    perm_scan_kernel<<<1, 1024, 0, s>>>(scratch, nchunks, E, offsets, tiles, num_tiles, tile_rows);
     if (nchunks > 0) perm_scatter_kernel<<<nchunks, 64, 0, s>>>(idx, P, E, scratch, sorted_pairs, pair_pos);
     return hipGetLastError();
 }

@@ -122,7 +122,10 @@ def test_permute_matches_oracle_counting_sort():
     import torch
     import sparse_moe_layer_04_amd as bm
     rng = np.random.default_rng(7)
-    for T, K, E in ((1, 8, 256), (64, 8, 256), (1000, 8, 64), (6000, 8, 256), (9000, 3, 1000)):
+    # one chunk of pairs (P <= 1024: a single work-group), exactly one full chunk, one pair
+    # over it, and several chunks
+    for T, K, E in ((1, 8, 256), (64, 8, 256), (128, 8, 256), (100, 10, 1024), (205, 5, 1000), (1000, 8, 64),
+                    (6000, 8, 256), (9000, 3, 1000)):
         # a skewed assignment with empty experts
         idx = np.minimum(rng.zipf(1.3, size=(T, K)) - 1, E - 1).astype(np.int32)
         shape = bm.make_shape(T, 128, E, 128, 1, 1, K, 1.0, "bf16")
