@@ -54,13 +54,22 @@ __global__ void __launch_bounds__(CMB_MAX_THREADS) combine_bf16_kernel(const uin
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-        for (int j = 0; j < K; ++j) {
-            const u32x4 v = *(const u32x4*)(y_pair + ((t * K + j) * H + c * 8));
-            const float wj = wk[j];
+        // up to eight expert rows in flight, then added in j order
+        for (int j0 = 0; j0 < K; j0 += 8) {
+            u32x4 v[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = fmaf(wj, __uint_as_float(v[q] << 16), acc[2 * q]);
-                acc[2 * q + 1] = fmaf(wj, __uint_as_float(v[q] & 0xFFFF0000u), acc[2 * q + 1]);
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u < K) v[u] = *(const u32x4*)(y_pair + ((t * K + j0 + u) * H + c * 8));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u < K) {
+                    const float wj = wk[j0 + u];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = fmaf(wj, __uint_as_float(v[u][q] << 16), acc[2 * q]);
+                        acc[2 * q + 1] = fmaf(wj, __uint_as_float(v[u][q] & 0xFFFF0000u), acc[2 * q + 1]);
+                    }
+                }
             }
         }
         u32x4 o;
