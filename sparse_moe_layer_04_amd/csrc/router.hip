@@ -169,12 +169,13 @@ static int router_rb(int64_t T) { return T >= RL_WIDE_MIN_T ? 8 : 4; }
 int router_splits(int64_t T, int H, int E) {
     const int rb = router_rb(T), tok = 16 * rb, exp = 512 / rb;
     const int64_t tiles = ((T + tok - 1) / tok) * ((E + exp - 1) / exp);
-    // up to ~1024 work-groups, each taking at least two units (four 32-k steps): more splits
-    // add fp64 partials that the selection must read back (at T = 300, 49 MB at 80 splits)
+    // up to ~512 work-groups (two per CU), each taking at least two units (four 32-k
+    // steps): more splits add fp64 partials that the selection must read back (at T = 300,
+    // 49 MB at 80 splits); a target of 1024 or 256 groups measured slower from T = 1000 on
     const int units = H / RL_KUNIT;
     int best = 1;
     for (int d = 1; 2 * d <= units; ++d)
-        if (units % d == 0 && tiles * d <= 1024) best = d;
+        if (units % d == 0 && tiles * d <= 512) best = d;
     return best;
 }
 
