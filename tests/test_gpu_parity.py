@@ -10,8 +10,8 @@ import oracle
 import synth
 from synth.configs import CONFIGS, make_inputs
 
-from moe_cases import (MID_CASES, DeviceInputs, as_f64, assert_routing_equal, dev, host, rel_err, run_forward,
-                       shape_of, tie_free_inputs)
+from moe_cases import (MID_CASES, DeviceInputs, as_f64, assert_routing_equal, dev, host, mid_config, rel_err,
+                       run_forward, shape_of, tie_free_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,12 +52,17 @@ def test_mid_layer_all_tokens(name):
 
 
 # 128-token router tiles (T >= 128) with ragged tails of 104, 72 and 1 rows, and 64-token
-# tiles (T = 80); 64, 1024 and 32 experts
-@pytest.mark.parametrize("name", ["mid_prefill_t1000", "mid_serve_t80", "mid_maxshape_t200", "mid_h1024_t257"])
+# tiles (T = 80); 64, 1024 and 32 experts; either side of the tile switch (T = 127, 128)
+ROUTE_CASES = dict(MID_CASES, route_t127=mid_config("route_t127", 127, seed_base=40000),
+                   route_t128=mid_config("route_t128", 128, seed_base=41000))
+
+
+@pytest.mark.parametrize("name", ["mid_prefill_t1000", "mid_serve_t80", "mid_maxshape_t200", "mid_h1024_t257",
+                                  "route_t127", "route_t128"])
 def test_route_logits_and_selection(name):
     import torch
     import sparse_moe_layer_04_amd as bm
-    cfg = MID_CASES[name]
+    cfg = ROUTE_CASES[name]
     inp = tie_free_inputs(cfg)
     ref = oracle.route(inp.x, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho,
                        want_logits=True)
