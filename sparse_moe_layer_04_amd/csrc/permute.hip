@@ -53,10 +53,16 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
     const int e = tid % E, g = tid / E;
     const int cpg = (nchunks + G - 1) / G;
     const int c0 = g * cpg, c1 = (g + 1) * cpg < nchunks ? (g + 1) * cpg : nchunks;
-    // (1) sum of each chunk range
+    // (1) sum of each chunk range (eight count rows in flight)
     if (g < G) {
         int32_t sum = 0;
-        for (int c = c0; c < c1; ++c) sum += counts[(int64_t)c * E + e];
+        for (int cb = c0; cb < c1; cb += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = cb + u < c1 ? counts[(int64_t)(cb + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
         part[g * E + e] = sum;
     }
     __syncthreads();
@@ -107,10 +113,16 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
     // (4) every chunk's first row per expert: expert offset + earlier chunks' counts
     if (g < G) {
         int32_t run = off[e] + part[g * E + e];
-        for (int c = c0; c < c1; ++c) {
-            const int32_t v = counts[(int64_t)c * E + e];
-            counts[(int64_t)c * E + e] = run;
-            run += v;
+        for (int cb = c0; cb < c1; cb += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = cb + u < c1 ? counts[(int64_t)(cb + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (cb + u < c1) {
+                    counts[(int64_t)(cb + u) * E + e] = run;
+                    run += v[u];
+                }
         }
     }
     // (5) expert offsets and the balanced tile list
@@ -140,15 +152,27 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ c
     perm_scan_body(counts, nchunks, E, offsets, tiles, num_tiles, tile_rows);
 }
 
-// One wave places the 64 pairs [pb, pb + 64) of a chunk ending at p1: lanes with equal
-// experts are ranked by ballots in pair order, and `next` holds each expert's next row.
-// The caller makes the cursor updates visible (a barrier) before the next 64 pairs.
-__device__ __forceinline__ void perm_scatter_step(const int32_t* __restrict__ idx, int64_t pb, int64_t p1, int E,
-                                                  int ebits, int32_t* next, int32_t* __restrict__ sorted_pairs,
-                                                  int32_t* __restrict__ pair_pos, int lane) {
+// The expert ids of a chunk's pairs, 64 per slice: lane l holds pair p0 + 64 s + l of
+// slice s (-1 past p1), all loaded before the ranking starts.
+constexpr int PERM_SLICES = PERM_CHUNK / 64;
+__device__ __forceinline__ void perm_load_ids(const int32_t* __restrict__ idx, int64_t p0, int64_t p1, int lane,
+                                              int (&ev)[PERM_SLICES]) {
+#pragma unroll
+    for (int sl = 0; sl < PERM_SLICES; ++sl) {
+        const int64_t p = p0 + sl * 64 + lane;
+        ev[sl] = p < p1 ? idx[p] : -1;
+    }
+}
+
+// One wave places the 64 pairs [pb, pb + 64) whose expert ids the lanes hold in `e` (-1
+// past the end): lanes with equal experts are ranked by ballots in pair order, and `next`
+// holds each expert's next row.  The caller makes the cursor updates visible (a barrier)
+// before the next 64 pairs.
+__device__ __forceinline__ void perm_scatter_step(int e, int64_t pb, int E, int ebits, int32_t* next,
+                                                  int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+                                                  int lane) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int64_t p = pb + lane;
-    int e = p < p1 ? idx[p] : -1;
     const bool valid = e >= 0 && e < E;  // out-of-range ids are skipped
     if (!valid) e = 0;
     uint64_t peers = __ballot(valid);
@@ -184,8 +208,12 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
     const int ebits = perm_ebits(E);
     const int64_t p0 = (int64_t)blockIdx.x * PERM_CHUNK;
     const int64_t p1 = p0 + PERM_CHUNK < P ? p0 + PERM_CHUNK : P;
-    for (int64_t pb = p0; pb < p1; pb += 64) {
-        perm_scatter_step(idx, pb, p1, E, ebits, next, sorted_pairs, pair_pos, lane);
+    int ev[PERM_SLICES];
+    perm_load_ids(idx, p0, p1, lane, ev);
+#pragma unroll
+    for (int sl = 0; sl < PERM_SLICES; ++sl) {
+        if (p0 + sl * 64 >= p1) break;   // uniform
+        perm_scatter_step(ev[sl], p0 + sl * 64, E, ebits, next, sorted_pairs, pair_pos, lane);
         __syncthreads();
     }
 }
@@ -204,6 +232,8 @@ __global__ void __launch_bounds__(1024) perm_single_kernel(const int32_t* __rest
     __shared__ int32_t cnt[PERM_MAX_E];
     __shared__ int32_t next[PERM_MAX_E];
     const int tid = threadIdx.x;
+    int ev[PERM_SLICES];   // wave 0's ids for the scatter, in flight during the count and scan
+    if (tid < 64) perm_load_ids(idx, 0, P, tid, ev);
     for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
     if (tid < P) {
@@ -218,8 +248,10 @@ __global__ void __launch_bounds__(1024) perm_single_kernel(const int32_t* __rest
     for (int e = tid; e < E; e += 1024) next[e] = counts[e];
     __syncthreads();
     const int ebits = perm_ebits(E);
-    for (int64_t pb = 0; pb < P; pb += 64) {
-        if (tid < 64) perm_scatter_step(idx, pb, P, E, ebits, next, sorted_pairs, pair_pos, tid);
+#pragma unroll
+    for (int sl = 0; sl < PERM_SLICES; ++sl) {
+        if (sl * 64 >= P) break;   // uniform
+        if (tid < 64) perm_scatter_step(ev[sl], sl * 64, E, ebits, next, sorted_pairs, pair_pos, tid);
         __syncthreads();
     }
 }
