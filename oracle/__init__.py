@@ -61,6 +61,8 @@ def _load():
         lib.oracle_post_residual.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -68,6 +70,11 @@ def _load():
 def threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP loops (the arithmetic does not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _is_bf16(a: np.ndarray) -> int:

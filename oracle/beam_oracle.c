@@ -354,3 +354,6 @@ void oracle_post_residual(const double* y, const void* x, int x_bf16, const floa
 
 /* threads the oracle's parallel loops use */
 int oracle_threads(void) { return omp_get_max_threads(); }
+
+/* sets the number of threads of the oracle's later parallel loops (n >= 1) */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

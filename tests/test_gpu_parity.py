@@ -194,3 +194,63 @@ def test_identical_experts_closed_form():
     single = oracle.experts(inp.x, inp.w_gate[:1].copy(), inp.w_up[:1].copy(), inp.w_down[:1].copy(), one,
                             np.full((cfg.T, 1), cfg.rho))
     assert rel_err(as_f64(got["out"]), single) <= 1e-2
+
+
+def _tie_tokens(H=256, E=256):
+    """Three tokens whose logits are exact: x = e_t and W_r[:, t] = the token's logits (bf16
+    1.0 times an fp32 weight is the weight).  Beam routing shape: 8 groups of 32, keep 4, top 8.
+    t0: every logit equal.  t1: exact ties inside the top 8 (33 = 40, 170 = 200) and at the
+    8th/9th place (180 = 202).  t2: groups 3 and 4 tie for the 4th place (the same two scores),
+    and group 4 holds an expert (128) above the last one chosen (96).
+    Ties go to the lower id (groups and experts alike); ids are listed in decision order."""
+    wr = np.zeros((E, H), np.float32)
+    col1 = np.full(E, -4.0, np.float32)
+    for e, v in {33: 3.0, 40: 3.0, 70: 2.0, 71: 1.5, 170: 1.0, 200: 1.0, 201: 0.5, 180: 0.25, 202: 0.25}.items():
+        col1[e] = v
+    col2 = np.full(E, -4.0, np.float32)
+    for e, v in {0: 2.0, 1: 2.0, 64: 1.5, 65: 1.5, 96: 0.5, 97: 1.0, 128: 1.0, 129: 0.5, 192: 1.8,
+                 193: 1.8}.items():
+        col2[e] = v
+    wr[:, 1] = col1
+    wr[:, 2] = col2
+    x = np.zeros((3, H), np.float32)
+    x[1, 1] = 1.0
+    x[2, 2] = 1.0
+    expected = [list(range(8)), [33, 40, 70, 71, 170, 200, 201, 180], [0, 1, 192, 193, 64, 65, 97, 96]]
+    return synth.f32_to_bf16(x), wr, expected
+
+
+def test_route_exact_ties_go_to_lower_id_on_gpu():
+    import torch
+    import sparse_moe_layer_04_amd as bm
+    H, E, I = 256, 256, 128
+    xb, wr, expected = _tie_tokens(H, E)
+    bias = np.zeros(E, np.float32)
+    ref = oracle.route(xb, wr, bias, 8, 4, 8, 2.5)
+    assert ref.idx.tolist() == expected      # the oracle reads ties the same way
+    shape = bm.make_shape(3, H, E, I, 8, 4, 8, 2.5, "bf16")
+    idx = torch.empty((3, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((3, 8), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bm.workspace_size(shape, bm.OP_ROUTE), dtype=torch.uint8, device="cuda")
+    bm.route(shape, dev(xb), dev(wr), dev(bias), idx, w, ws=ws)
+    torch.cuda.synchronize()
+    assert host(idx).tolist() == expected    # decision order and set
+    np.testing.assert_allclose(host(w), ref.w, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(host(w)[0], [2.5 / 8] * 8, rtol=1e-7, atol=0)
+    # the whole layer takes the same decisions
+    rng = np.random.default_rng(7)
+    wg = synth.f32_to_bf16((rng.standard_normal((E, I, H)) * 0.05).astype(np.float32))
+    wu = synth.f32_to_bf16((rng.standard_normal((E, I, H)) * 0.05).astype(np.float32))
+    wd = synth.f32_to_bf16((rng.standard_normal((E, H, I)) * 0.05).astype(np.float32))
+    out = torch.empty((3, H), dtype=torch.bfloat16, device="cuda")
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    wsf = torch.empty(bm.workspace_size(shape, bm.OP_FORWARD), dtype=torch.uint8, device="cuda")
+    bm.forward(shape, dev(xb), dev(wr), dev(bias), dev(wg), dev(wu), dev(wd), out, wsf, topk_idx=idx2, topk_w=w2)
+    torch.cuda.synchronize()
+    assert host(idx2).tolist() == expected
+    assert torch.equal(w, w2)
+    y = oracle.experts(xb, wg, wu, wd, ref.idx, ref.w)
+    err = rel_err(as_f64(host(out)), y)
+    print("tie tokens: layer rel err %.3e" % err)
+    assert err <= 1e-2

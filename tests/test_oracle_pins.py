@@ -66,6 +66,43 @@ def test_route_known_scores_fixture():
         assert r.idx[0].tolist() == fx["expected_idx"]
         np.testing.assert_allclose(r.w[0], fx["expected_w"], rtol=2e-7)
         assert abs(r.w[0].sum() - fx["rho"]) < 1e-12
+        # distance to the nearest tie: the scores are n/32 up to the fp32 rounding of the logits
+        np.testing.assert_allclose(r.margin[0], fx["expected_margin"], rtol=0, atol=1e-6)
+        assert r.agree[0] == 1
+
+
+def _margins_by_definition(sb, n_group, topk_group, top_k):
+    """fp64 distance to the nearest tie, from the biased scores sb [T,E]: the last kept group
+    score minus the first dropped one, and the top_k-th biased score among the experts of the
+    kept groups minus the next one (inf where nothing is dropped)."""
+    T, E = sb.shape
+    gsz = E // n_group
+    out = np.full((T, 2), np.inf)
+    for t in range(T):
+        top2 = np.sort(sb[t].reshape(n_group, gsz), axis=1)[:, ::-1][:, :2].sum(1)
+        order = np.argsort(-top2, kind="stable")
+        if topk_group < n_group:
+            out[t, 0] = top2[order[topk_group - 1]] - top2[order[topk_group]]
+        cand = np.sort(np.concatenate([sb[t, g * gsz:(g + 1) * gsz] for g in order[:topk_group]]))[::-1]
+        if cand.size > top_k:
+            out[t, 1] = cand[top_k - 1] - cand[top_k]
+    return out
+
+
+@pytest.mark.parametrize("name,j", [("tiny_f32", 0), ("tiny_f32", 1), ("tiny_f32", 2), ("decode_t64", 0)])
+def test_route_margins_match_their_definition(name, j):
+    # the margins decide which seeds count as tie-free for every parity test: recompute them
+    # from the oracle's fp64 logits with numpy sorts and compare
+    cfg = CONFIGS[name]
+    if cfg.H > 1024:   # the Beam router shape at a few tokens (routing does not read the experts)
+        cfg = cfg.replace(T=8, I=16)
+    inp = make_inputs(cfg, j=j)
+    r = oracle.route(inp.x, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho,
+                     want_logits=True)
+    sb = _sig(r.logits) + inp.bias.astype(np.float64)[None, :]
+    np.testing.assert_allclose(r.margin, _margins_by_definition(sb, cfg.n_group, cfg.topk_group, cfg.top_k),
+                               rtol=0, atol=1e-12)
+    assert (r.margin > 0).all()
 
 
 def test_route_bias_dominated_fixture_and_masking():
