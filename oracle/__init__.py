@@ -57,6 +57,8 @@ def _load():
         lib.oracle_e4m3_value.restype = f64
         lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e2m1_value.restype = f64
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = f64
         lib.oracle_post_residual.argtypes = [vp, vp, i32, vp, f32, i64, i64, f64, vp]
         lib.oracle_post_residual.restype = None
         lib.oracle_threads.argtypes = []
@@ -140,6 +142,11 @@ def route(act: np.ndarray, w_router: np.ndarray, bias: np.ndarray, n_group: int,
 def e4m3_value(code: int) -> float:
     """The value of one OCP FP8 E4M3 code (the oracle's decoding)."""
     return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e8m0_value(s: int) -> float:
+    """The factor of one E8M0 scale byte, 0..255 (the oracle's decoding)."""
+    return float(_load().oracle_e8m0_value(int(s)))
 
 
 def e2m1_value(code: int) -> float:

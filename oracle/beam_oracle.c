@@ -97,13 +97,17 @@ double oracle_e2m1_value(uint8_t code) {
     return sgn ? -v : v;
 }
 
+/* value of one E8M0 scale byte (OCP microscaling formats): an exponent alone with bias
+ * 127, 2^(s - 127) for s = 0 .. 254 (0 is 2^-127: no zero), and 0xFF is NaN (no infinity) */
+double oracle_e8m0_value(uint8_t s) { return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127); }
+
 /* decoding tables for one call: value of every code and factor of every scale byte */
 typedef struct { double code[256], fp4[16], scale[256]; } fp8_tables;
 
 static void fp8_tables_init(fp8_tables* t) {
     for (int i = 0; i < 256; ++i) {
         t->code[i] = oracle_e4m3_value((uint8_t)i);
-        t->scale[i] = ldexp(1.0, i - 127);
+        t->scale[i] = oracle_e8m0_value((uint8_t)i);
     }
     for (int i = 0; i < 16; ++i) t->fp4[i] = oracle_e2m1_value((uint8_t)i);
 }

@@ -32,7 +32,9 @@ MUTANTS = {
     "e4m3_exponent_bias_8": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
     "e4m3_subnormal_as_normal": ("e == 0 ? ldexp((double)m, -9)", "e == 0 ? ldexp(1.0 + m / 8.0, -7)"),
     "e4m3_mantissa_4_bits": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 16.0, e - 7)"),
-    "e8m0_scale_bias": ("t->scale[i] = ldexp(1.0, i - 127);", "t->scale[i] = ldexp(1.0, i - 128);"),
+    "e8m0_scale_bias": ("ldexp(1.0, (int)s - 127); }", "ldexp(1.0, (int)s - 128); }"),
+    "e8m0_no_nan": ("return s == 0xFF ? NAN : ldexp", "return s == 0x100 ? NAN : ldexp"),
+    "e8m0_zero_byte_is_zero": ("return s == 0xFF ? NAN : ldexp", "return s == 0 ? 0.0 : s == 0xFF ? NAN : ldexp"),
     "scale_block_of_16": ("t->code[((const uint8_t*)p)[i]] * t->scale[sc[i >> 5]]",
                           "t->code[((const uint8_t*)p)[i]] * t->scale[sc[i >> 4]]"),
     "e2m1_exponent_bias_2": ("ldexp(1.0 + m / 2.0, e - 1)", "ldexp(1.0 + m / 2.0, e - 2)"),

@@ -514,6 +514,45 @@ def test_fp8_layer_equals_the_layer_on_the_decoded_weights():
     assert not np.allclose(y_bad, y_fp8)
 
 
+def test_e8m0_values_fixed_by_the_format():
+    # OCP microscaling specification, E8M0 scale: an 8-bit exponent with bias 127 and no
+    # sign or mantissa; 0x00 is 2^-127 (there is no zero), 0xFF is NaN (no infinity)
+    assert oracle.e8m0_value(127) == 1.0
+    assert oracle.e8m0_value(128) == 2.0 and oracle.e8m0_value(126) == 0.5
+    assert oracle.e8m0_value(0) == math.ldexp(1.0, -127)
+    assert oracle.e8m0_value(254) == math.ldexp(1.0, 127)
+    assert math.isnan(oracle.e8m0_value(255))
+    for s in range(255):
+        assert oracle.e8m0_value(s) == math.ldexp(1.0, s - 127)
+
+
+def test_e8m0_edge_bytes_reach_the_expert_path():
+    # a block scaled by byte 0 gives its codes times 2^-127; a NaN scale makes the output NaN
+    H, I, E, T = 64, 32, 2, 3
+    rng = np.random.default_rng(5)
+    codes = np.full((E, I, H), 0x40, np.uint8)          # E4M3 2.0
+    cd = np.full((E, H, I), 0x38, np.uint8)             # E4M3 1.0
+    sg = np.full((E, I, H // 32), 127, np.uint8)
+    sd = np.full((E, H, I // 32), 127, np.uint8)
+    u = synth.f32_to_bf16(rng.normal(size=(T, H)).astype(np.float32))
+    idx = np.zeros((T, 1), np.int32)
+    wts = np.ones((T, 1))
+    y = oracle.experts(u, codes, codes, cd, idx, wts, w_scales=(sg, sg, sd))
+    su = sg.copy()
+    su[0, :, 0] = 0                                     # up rows: first block scaled by 2^-127
+    ub = synth.bf16_to_f32(u).astype(np.float64)
+    a = 2.0 * ub.sum(1)                                 # gate rows: 2 * sum(u)
+    c = 2.0 * ub[:, 32:].sum(1) + 2.0 * math.ldexp(1.0, -127) * ub[:, :32].sum(1)
+    h = a / (1.0 + np.exp(-a)) * c
+    y0 = oracle.experts(u, codes, codes, cd, idx, wts, w_scales=(sg, su, sd))
+    np.testing.assert_allclose(y0, np.repeat((I * h)[:, None], H, 1), rtol=1e-12)
+    assert not np.allclose(y0, y)
+    sn = sd.copy()
+    sn[0, 5, 0] = 255                                   # one NaN scale in output row 5 of expert 0
+    yn = oracle.experts(u, codes, codes, cd, idx, wts, w_scales=(sg, sg, sn))
+    assert np.isnan(yn[:, 5]).all() and np.isfinite(np.delete(yn, 5, axis=1)).all()
+
+
 def test_e2m1_values_fixed_by_the_format():
     # OCP microscaling specification, FP4 E2M1: bias 1, magnitudes 0, 0.5 (the one
     # subnormal), 1, 1.5, 2, 3, 4, 6 (the largest); bit 3 is the sign; no infinities or NaN
