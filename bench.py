@@ -3,8 +3,15 @@
 
 A step is one ``beam_moe_forward`` call (router -> permutation -> gate/up -> down ->
 combine) over one batch of synthetic, seeded tokens already resident in HBM.  The primary
-line is the 8192-token prefill layer; the same run also times the 64-token decode layer
-(``secondary``).  Prints ONE JSON line.
+line is the 8192-token prefill layer; the same run times the other four workloads (the
+tiny fp32 layer, the 64-token decode layer, the skewed 6000-token layer and the 32768-token
+sublayer), the decode and prefill layers with 8-bit and 4-bit expert weights, and the CPU
+oracle as a baseline.  Prints ONE JSON line.
+
+Timing: W untimed warm-up steps, then K bare forwards, each bracketed by events on the
+launch stream (``ms_per_step`` is their median; the bracket around all K gives the mean);
+the per-stage times come from a separate pass whose forwards record events at every stage
+boundary on the same stream.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prefill_t8192]
   python bench.py --sweep 16,64,256,1024 [--sweep-md table.md]   # serving shapes, one line per size
@@ -17,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -27,7 +35,12 @@ METRIC = "MoE-layer tokens/s at 1 MI355X (prefill 8192 / decode 64); % MFMA / HB
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-EXPERTS_SRC = os.path.join(ROOT, "sparse_moe_layer_04_amd", "csrc", "experts.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "sparse_moe_layer_04_amd", "csrc", "experts.hip")]
+EXPERTS_SRC = GEMM_SOURCES[0]
+# the workloads timed besides the primary one, in this order
+OTHER_WORKLOADS = ("tiny_f32", "decode_t64", "skew_t6000", "sublayer_t32768")
+CPU_SUBSET = 256            # seeded token subset of the oracle baseline for the large workloads
+CPU_ONE_THREAD_TOKENS = 8   # prefill tokens of the one-thread oracle figure
 
 
 def log(*a):
@@ -35,12 +48,15 @@ def log(*a):
 
 
 def kernel_source_hash(text=None) -> str:
-    """Hash of the expert-GEMM source with its comments and blank space removed, so that a
+    """Hash of the expert-GEMM sources with their comments and blank space removed, so that a
     change to the comments alone keeps recorded counter traffic valid."""
     import re
     if text is None:
-        with open(EXPERTS_SRC) as f:
-            text = f.read()
+        parts = []
+        for p in GEMM_SOURCES:
+            with open(p) as f:
+                parts.append(f.read())
+        text = "\n".join(parts)
     code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     code = re.sub(r"//[^\n]*", " ", code)
     code = " ".join(code.split())
@@ -48,9 +64,15 @@ def kernel_source_hash(text=None) -> str:
 
 
 def weight_bytes_per_element(cfg):
-    """bf16: 2; 8-bit storage: 1 byte per code plus one scale byte per 32 elements; MXFP4:
-    half a byte per code plus the scale byte per 32."""
+    """bf16: 2; fp32: 4; 8-bit storage: 1 byte per code plus one scale byte per 32 elements;
+    MXFP4: half a byte per code plus the scale byte per 32."""
+    if cfg.dtype == "f32":
+        return 4.0
     return {"fp8": 1.0 + 1.0 / 32, "mxfp4": 0.5 + 1.0 / 32}.get(cfg.weights, 2.0)
+
+
+def act_bytes(cfg):
+    return 4.0 if cfg.dtype == "f32" else 2.0
 
 
 def gate_up_work(cfg, n_touched):
@@ -58,10 +80,11 @@ def gate_up_work(cfg, n_touched):
 
     flops: 4*H*I per routed pair (gate and up products).
     bytes: each touched expert's gate and up matrices once (2*I*H weights), each token row
-    once (H bf16), each h row written once (I bf16)."""
+    once (H activations), each h row written once (I activations)."""
     P = cfg.T * cfg.top_k
+    a = act_bytes(cfg)
     flops = 4.0 * cfg.H * cfg.I * P
-    nbytes = n_touched * 2.0 * cfg.I * cfg.H * weight_bytes_per_element(cfg) + cfg.T * cfg.H * 2.0 + P * cfg.I * 2.0
+    nbytes = n_touched * 2.0 * cfg.I * cfg.H * weight_bytes_per_element(cfg) + cfg.T * cfg.H * a + P * cfg.I * a
     return flops, nbytes
 
 
@@ -69,7 +92,17 @@ def down_work(cfg, n_touched):
     """flops 2*H*I per pair; bytes: each touched W_d once, each h row read, each output row written."""
     P = cfg.T * cfg.top_k
     return (2.0 * cfg.H * cfg.I * P,
-            n_touched * cfg.H * cfg.I * weight_bytes_per_element(cfg) + P * (cfg.I + cfg.H) * 2.0)
+            n_touched * cfg.H * cfg.I * weight_bytes_per_element(cfg) + P * (cfg.I + cfg.H) * act_bytes(cfg))
+
+
+def layer_work(cfg, n_touched):
+    """Whole-layer flops (6*H*I per pair; the router's 2*E*H per token excluded) and
+    algorithmic bytes (touched experts' weights, W_r, x in, out)."""
+    P = cfg.T * cfg.top_k
+    flops = 6.0 * cfg.H * cfg.I * P
+    nbytes = (n_touched * 3.0 * cfg.H * cfg.I * weight_bytes_per_element(cfg) + cfg.E * cfg.H * 4.0 +
+              2.0 * cfg.T * cfg.H * act_bytes(cfg))
+    return flops, nbytes
 
 
 def roofline(flops, nbytes, seconds, traffic=None):
@@ -100,7 +133,7 @@ def load_traffic(workload, kernel):
         return None
 
 
-# expert GEMM kernels (the decode kernel or the line-streaming kernel) by their GATED template flag
+# expert GEMM kernels (the decode, line or prefill kernel) by their GATED template flag
 KERNEL_NAMES = {"gate_up": "<true", "down": "<false"}
 
 
@@ -147,32 +180,47 @@ def ingest_counters(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write
     print(json.dumps({workload: ent}))
 
 
-def run_workload(cfg, hw, dw, steps, warmup, scales=None):
-    """Times `steps` layers of workload `cfg` (weights hw on the host, dw on the device; for
-    8-bit weights `scales` = (host scales, device scales))."""
+def expert_histogram(counts):
+    """The per-expert routed-row counts of a step: touched, min, median, max, empty, top-8."""
+    import numpy as np
+    c = np.asarray(counts)
+    return {"touched": int((c > 0).sum()), "min": int(c.min()), "median": float(np.median(c)),
+            "max": int(c.max()), "empty": int((c == 0).sum()),
+            "top8": [int(v) for v in np.sort(c)[::-1][:8]]}
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_workload(cfg, hw, dw, steps, warmup, scales=None, stage_steps=None):
+    """Times workload `cfg` (weights hw on the host, dw on the device; quantized weights come
+    with `scales` = (host scales, device scales)).
+
+    K = `steps` bare forwards, each between two events on the launch stream, give the median
+    and mean step times; a separate pass of `stage_steps` forwards records the stage events."""
     import numpy as np
     import torch
 
     import sparse_moe_layer_04_amd as bm
     from synth.configs import make_inputs
 
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
     inp = make_inputs(cfg, weights=hw, w_scales=scales[0] if scales else None)
     shape = bm.make_shape(cfg.T, cfg.H, cfg.E, cfg.I, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, cfg.dtype)
     op = bm.OP_FORWARD_SUBLAYER if cfg.sublayer else bm.OP_FORWARD
     ws = torch.empty(bm.workspace_size(shape, op), dtype=torch.uint8, device="cuda")
-    x, bias = dev(inp.x), dev(inp.bias)
-    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    x, bias = _dev(inp.x), _dev(inp.bias)
+    act_dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    out = torch.empty((cfg.T, cfg.H), dtype=act_dt, device="cuda")
     idx = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device="cuda")
     sub = None
     if cfg.sublayer:
-        g1, g2 = dev(inp.pre_gain), dev(inp.post_gain)
+        g1, g2 = _dev(inp.pre_gain), _dev(inp.post_gain)
         sub = bm.sublayer(g1, g2, cfg.eps, cfg.residual_k)
-    timers = [bm.StageTimer() for _ in range(steps)]
 
     def step(timer=None):
         bm.forward(shape, x, dw[0], bias, dw[1], dw[2], dw[3], out, ws, sublayer=sub, topk_idx=idx,
@@ -182,68 +230,137 @@ def run_workload(cfg, hw, dw, steps, warmup, scales=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        step(timers[i])
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / steps
-    stage = np.array([t.elapsed_ms() for t in timers]).mean(axis=0)
+    per_step = [a.elapsed_time(b) for a, b in ev]
+    # stage pass
+    n_stage = steps if stage_steps is None else stage_steps
+    timers = [bm.StageTimer() for _ in range(n_stage)]
+    for t in timers:
+        step(t)
+    torch.cuda.synchronize()
+    stage = np.array([t.elapsed_ms() for t in timers])
     for t in timers:
         t.close()
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.E)
-    n_touched = int((counts > 0).sum())
-    return dict(ms_per_step=ms_per_step, wall_s=wall, stage_ms=stage, counts=counts, n_touched=n_touched)
+    return dict(ms_median=statistics.median(per_step), ms_mean=t_start.elapsed_time(t_end) / steps,
+                ms_min=min(per_step), wall_s=wall, stage_ms=stage.mean(axis=0), counts=counts,
+                n_touched=int((counts > 0).sum()))
 
 
-def summarize(cfg, r, steps, warmup):
-    ms = r["ms_per_step"]
-    P = cfg.T * cfg.top_k
+def summarize(cfg, r):
+    import sparse_moe_layer_04_amd as bm
+    ms = r["ms_median"]
     gu_ms = float(r["stage_ms"][4])
     dn_ms = float(r["stage_ms"][5])
     gu_f, gu_b = gate_up_work(cfg, r["n_touched"])
     dn_f, dn_b = down_work(cfg, r["n_touched"])
-    layer_flops = 6.0 * cfg.H * cfg.I * P
-    weight_bytes = r["n_touched"] * 3.0 * cfg.H * cfg.I * weight_bytes_per_element(cfg)
-    layer_bytes = weight_bytes + cfg.E * cfg.H * 4.0 + 2.0 * cfg.T * cfg.H * 2
-    import sparse_moe_layer_04_amd as bm
+    lf, lb = layer_work(cfg, r["n_touched"])
     return {
+        "workload": cfg.name,
+        "T": cfg.T,
         "tokens_per_s": cfg.T / (ms / 1e3),
         "ms_per_step": ms,
+        "ms_mean": r["ms_mean"],
+        "ms_min": r["ms_min"],
         "stages_ms": {n: round(float(v), 4) for n, v in zip(bm.STAGE_NAMES, r["stage_ms"])},
-        "layer": {"tflops": layer_flops / (ms / 1e3) / 1e12, "mfma_frac": layer_flops / (ms / 1e3) / 1e12 /
-                  PEAK_BF16_TFLOPS, "alg_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms / 1e3) / 1e9,
-                  "hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "layer": {"tflops": lf / (ms / 1e3) / 1e12, "mfma_frac": lf / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "alg_bytes": lb, "hbm_gbs": lb / (ms / 1e3) / 1e9,
+                  "hbm_frac": lb / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "gate_up": roofline(gu_f, gu_b, gu_ms / 1e3, load_traffic(cfg.name, "gate_up")),
         "down": roofline(dn_f, dn_b, dn_ms / 1e3, load_traffic(cfg.name, "down")),
-        "experts_touched": r["n_touched"],
-        "max_expert_load": int(r["counts"].max()),
-        "empty_experts": int((r["counts"] == 0).sum()),
+        "experts": expert_histogram(r["counts"]),
     }
 
 
-def cpu_baseline(cfg, hw, n_tokens, w_scales=None):
-    """The oracle, as it stands, on a seeded sample of the workload's tokens."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_pass(cfg, inp, tok):
+    """The oracle on the tokens `tok` of a workload: pre-norm (sublayer), router, experts,
+    post-norm and residual (sublayer); returns the seconds it took."""
+    import numpy as np
     import oracle
-    import synth
-    from synth.configs import make_inputs
-    inp = make_inputs(cfg, weights=hw, w_scales=w_scales)
-    tok = synth.subset(cfg.seed_base + 555, 98, cfg.T, n_tokens)
     t0 = time.perf_counter()
-    x = inp.x[tok]
+    x = np.ascontiguousarray(inp.x[tok])
     u = oracle.rmsnorm_pinned(x, inp.pre_gain, cfg.eps) if cfg.sublayer else x
     r = oracle.route(u, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, want_margin=False)
     y = oracle.experts(u, inp.w_gate, inp.w_up, inp.w_down, r.idx, r.w, w_scales=inp.w_scales)
     if cfg.sublayer:
         oracle.post_residual(y, x, inp.post_gain, cfg.eps, cfg.residual_k)
-    dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "%d seeded tokens of %s (router + experts%s), %.1f s" % (
-                n_tokens, cfg.name, " + norms" if cfg.sublayer else "", dt)}
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(primary, hw, others=(), one_thread=True, w_scales=None):
+    """The oracle as it stands, on the host's cores: every token of the tiny and the decode
+    workloads, a seeded 256-token subset of the larger ones (router and experts on the
+    subset), the router alone over every token of each workload, and a one-thread figure on
+    a few prefill tokens.  The primary workload's subset gives `value`."""
+    import numpy as np
+    import oracle
+    import synth
+    from synth.configs import CONFIGS, make_inputs
+    threads = oracle.threads()
+    per = {}
+    router_all = {}
+    inputs = {}
+    names = [primary.name] + [n for n in others if n != primary.name]
+    for name in names:
+        cfg = CONFIGS[name]
+        inp = make_inputs(cfg, weights=None if cfg.dtype == "f32" else hw,
+                          w_scales=w_scales if name == primary.name else None)
+        inputs[name] = inp
+        if cfg.T <= 64:
+            tok = np.arange(cfg.T, dtype=np.int64)
+            kind = "all %d tokens" % cfg.T
+        else:
+            tok = synth.subset(cfg.seed_base + 555, 98, cfg.T, CPU_SUBSET)
+            kind = "%d seeded tokens of %d" % (CPU_SUBSET, cfg.T)
+        dt = _oracle_pass(cfg, inp, tok)
+        per[name] = {"tokens": int(tok.size), "seconds": dt, "tokens_per_s": tok.size / dt, "sample": kind}
+        log("cpu oracle %s: %s in %.1f s" % (name, kind, dt))
+        t0 = time.perf_counter()
+        u = oracle.rmsnorm_pinned(inp.x, inp.pre_gain, cfg.eps) if cfg.sublayer else inp.x
+        oracle.route(u, inp.w_router, inp.bias, cfg.n_group, cfg.topk_group, cfg.top_k, cfg.rho, want_margin=False)
+        dt = time.perf_counter() - t0
+        router_all[name] = {"tokens": cfg.T, "seconds": dt, "tokens_per_s": cfg.T / dt}
+    one = None
+    if one_thread:
+        cfg = primary
+        tok = synth.subset(cfg.seed_base + 556, 98, cfg.T, CPU_ONE_THREAD_TOKENS)
+        oracle.set_threads(1)
+        try:
+            dt = _oracle_pass(cfg, inputs[cfg.name], tok)
+        finally:
+            oracle.set_threads(threads)
+        one = {"workload": cfg.name, "tokens": int(tok.size), "seconds": dt, "tokens_per_s": tok.size / dt,
+               "threads": 1}
+        log("cpu oracle one thread: %d tokens in %.1f s" % (tok.size, dt))
+    p = per[primary.name]
+    return {"value": p["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s of %s (%s), %.1f s" % (
+                p["sample"], primary.name,
+                "pre-norm, router, experts, post-norm" if primary.sublayer else "router and experts", p["seconds"]),
+            "cpu_model": cpu_model(), "per_workload": per, "router_only_all_tokens": router_all,
+            "one_thread": one}
 
 
 def sweep(base, hw, dw, sizes, steps, warmup, md_path="", scales=None):
@@ -253,10 +370,10 @@ def sweep(base, hw, dw, sizes, steps, warmup, md_path="", scales=None):
     for T in sizes:
         c = base.replace(name="serve_t%d" % T, T=T)
         r = run_workload(c, hw, dw, steps, warmup, scales=scales)
-        s = summarize(c, r, steps, warmup)
+        s = summarize(c, r)
         row = {"workload": c.name, "T": T, "tokens_per_s": s["tokens_per_s"], "ms_per_step": s["ms_per_step"],
                "gate_up_ms": s["stages_ms"]["gate_up"], "down_ms": s["stages_ms"]["down"],
-               "experts_touched": s["experts_touched"], "rows_per_expert": T * c.top_k / c.E,
+               "experts_touched": s["experts"]["touched"], "rows_per_expert": T * c.top_k / c.E,
                "mfma_frac": s["layer"]["mfma_frac"], "hbm_frac": s["layer"]["hbm_frac"]}
         rows.append(row)
         print(json.dumps(row), flush=True)
@@ -290,8 +407,8 @@ def main():
     ap.add_argument("--workload", default="prefill_t8192",
                     choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768", "decode_t64_fp8",
                              "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4"])
-    ap.add_argument("--secondary", default="decode_t64", help="second workload timed in the same run, or 'none'")
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--secondary", default=",".join(OTHER_WORKLOADS),
+                    help="comma-separated workloads timed in the same run besides the primary one, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the decode and prefill layers with 8-bit and 4-bit expert weights")
@@ -320,25 +437,19 @@ def main():
         copy_calibration(args.copy_calib)
         return
     import sparse_moe_layer_04_amd  # noqa: F401  (fails loudly without the HIP library)
-    from synth.configs import CONFIGS, expert_weights
+    from synth.configs import CONFIGS, expert_weights, make_inputs
 
     cfg = CONFIGS[args.workload]
     t0 = time.time()
     hw = expert_weights(cfg)
     log("weights generated in %.1fs" % (time.time() - t0))
 
-    def dev(a):
-        import numpy as np
-        if a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
     scales = None
     if cfg.weights != "bf16":   # the primary workload reads quantized weights: quantize, keep only those
         from synth.configs import quantized_weights
         hw, hs = quantized_weights(cfg, hw)
-        scales = (hs, tuple(dev(a) for a in hs))
-    dw = tuple(dev(a) for a in hw)
+        scales = (hs, tuple(_dev(a) for a in hs))
+    dw = tuple(_dev(a) for a in hw)
     torch.cuda.synchronize()
     log("weights uploaded")
 
@@ -348,9 +459,10 @@ def main():
               scales=scales)
         return
 
+    bench_wall0 = time.perf_counter()
     prim = run_workload(cfg, hw, dw, args.steps, args.warmup, scales=scales)
-    s = summarize(cfg, prim, args.steps, args.warmup)
-    log("primary %s: %.3f ms/step" % (cfg.name, s["ms_per_step"]))
+    s = summarize(cfg, prim)
+    log("primary %s: %.3f ms/step (median), %.3f mean" % (cfg.name, s["ms_per_step"], s["ms_mean"]))
     line = {
         "metric": METRIC,
         "value": s["tokens_per_s"],
@@ -359,6 +471,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": s["ms_per_step"],
+        "ms_per_step_mean": s["ms_mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -368,23 +481,30 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "n_group": cfg.n_group,
                    "topk_group": cfg.topk_group, "top_k": cfg.top_k, "routed_scaling": cfg.rho,
                    "sublayer": cfg.sublayer, "parallelism": "single GPU"},
-        "roofline": dict(s["gate_up"], kernel="gate_up (grouped gate/up GEMM + SwiGLU)"),
+        "roofline": dict(s["gate_up"], kernel="gate_up (grouped gate/up GEMM + SwiGLU)",
+                         kernel_ms=s["stages_ms"]["gate_up"], kernel_ms_source="stage-event pass, mean"),
         "layer": s["layer"],
         "stages_ms": s["stages_ms"],
         "down": s["down"],
-        "experts_touched": s["experts_touched"],
-        "max_expert_load": s["max_expert_load"],
-        "empty_experts": s["empty_experts"],
+        "experts": s["experts"],
+        "gemm_code_sha256_16": kernel_source_hash(),
     }
-    if args.secondary and args.secondary != "none" and args.secondary != cfg.name and cfg.weights == "bf16":
-        c2 = CONFIGS[args.secondary]
-        r2 = run_workload(c2, hw, dw, args.steps, args.warmup)
-        s2 = summarize(c2, r2, args.steps, args.warmup)
-        log("secondary %s: %.3f ms/step" % (c2.name, s2["ms_per_step"]))
-        line["secondary"] = {"workload": c2.name, "tokens_per_s": s2["tokens_per_s"],
-                             "ms_per_step": s2["ms_per_step"], "layer": s2["layer"], "stages_ms": s2["stages_ms"],
-                             "roofline": dict(s2["gate_up"], kernel="gate_up"), "down": s2["down"],
-                             "experts_touched": s2["experts_touched"]}
+    others = [] if args.secondary == "none" else [n for n in args.secondary.split(",") if n and n != cfg.name]
+    if cfg.weights == "bf16" and others:
+        line["workloads"] = {}
+        for name in others:
+            c2 = CONFIGS[name]
+            if c2.dtype == "f32":   # the tiny fp32 layer has its own weights
+                hw2 = make_inputs(c2)
+                hw2 = (hw2.w_router, hw2.w_gate, hw2.w_up, hw2.w_down)
+                dw2 = tuple(_dev(a) for a in hw2)
+                r2 = run_workload(c2, hw2, dw2, args.steps, args.warmup)
+                del dw2
+            else:
+                r2 = run_workload(c2, hw, dw, args.steps, args.warmup)
+            s2 = summarize(c2, r2)
+            log("%s: %.3f ms/step" % (c2.name, s2["ms_per_step"]))
+            line["workloads"][c2.name] = s2
     del dw
     torch.cuda.empty_cache()
     if not args.no_fp8 and args.workload == "prefill_t8192":
@@ -395,22 +515,21 @@ def main():
         for fmt, key in (("fp8", "fp8_weights"), ("mxfp4", "mxfp4_weights")):
             names = ("decode_t64_" + fmt, "prefill_t8192_" + fmt)
             hq, hs = quantized_weights(CONFIGS[names[0]], hw)
-            dq, ds = tuple(dev(a) for a in hq), tuple(dev(a) for a in hs)
+            dq, ds = tuple(_dev(a) for a in hq), tuple(_dev(a) for a in hs)
             torch.cuda.synchronize()
             line[key] = {}
             for name in names:
                 c8 = CONFIGS[name]
                 r8 = run_workload(c8, hq, dq, args.steps, args.warmup, scales=(hs, ds))
-                s8 = summarize(c8, r8, args.steps, args.warmup)
+                s8 = summarize(c8, r8)
                 log("%s %s: %.3f ms/step" % (fmt, name, s8["ms_per_step"]))
-                line[key][name] = {"tokens_per_s": s8["tokens_per_s"], "ms_per_step": s8["ms_per_step"],
-                                   "layer": s8["layer"], "stages_ms": s8["stages_ms"],
-                                   "gate_up": s8["gate_up"], "down": s8["down"],
-                                   "experts_touched": s8["experts_touched"]}
+                line[key][name] = s8
             del dq, ds, hq, hs
             torch.cuda.empty_cache()
+    line["gpu_wall_s"] = time.perf_counter() - bench_wall0
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, hw, args.cpu_tokens, w_scales=scales[0] if scales else None)
+        line["cpu_baseline"] = cpu_baseline(cfg, hw, others=others if cfg.weights == "bf16" else (),
+                                            w_scales=scales[0] if scales else None)
     print(json.dumps(line), flush=True)
 
 

@@ -59,7 +59,9 @@ def test_code_hash_ignores_comments_and_blank_space_only():
     h = bench.kernel_source_hash(src)
     assert bench.kernel_source_hash("// header\n" + src.replace("    ", "  ") + "\n\n") == h
     assert bench.kernel_source_hash(src.replace("a + 1", "a + 2")) != h
-    assert bench.kernel_source_hash() == bench.kernel_source_hash(open(bench.EXPERTS_SRC).read())
+    # the recorded hash covers every expert-GEMM source
+    assert bench.kernel_source_hash() == bench.kernel_source_hash(
+        "\n".join(open(p).read() for p in bench.GEMM_SOURCES))
 
 
 def _pmc_csv(path, counter, rows):
@@ -95,3 +97,18 @@ def test_counter_ingestion_scales_by_the_copy_calibration(tmp_path, monkeypatch)
     json.dump(rec, open(tmp_path / "traffic.json", "w"))
     assert bench.load_traffic("prefill_t8192", "gate_up") is None
     assert bench.load_traffic("decode_t64", "gate_up") is None
+
+
+def test_expert_histogram():
+    h = bench.expert_histogram([0, 3, 5, 0, 9, 1, 2, 2, 7, 4])
+    assert h == {"touched": 8, "min": 0, "median": 2.5, "max": 9, "empty": 2, "top8": [9, 7, 5, 4, 3, 2, 2, 1]}
+
+
+def test_layer_work_counts_touched_experts_router_and_activations():
+    cfg = CONFIGS["prefill_t8192"]
+    f, b = bench.layer_work(cfg, 256)
+    assert f == 6.0 * 5120 * 2560 * 8192 * 8
+    assert b == 256 * 3.0 * 5120 * 2560 * 2 + 256 * 5120 * 4 + 2 * 8192 * 5120 * 2
+    tiny = CONFIGS["tiny_f32"]
+    f, b = bench.layer_work(tiny, 16)
+    assert b == 16 * 3.0 * 64 * 32 * 4 + 16 * 64 * 4 + 2 * 32 * 64 * 4     # fp32 weights and activations
