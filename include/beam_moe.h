@@ -192,12 +192,16 @@ beam_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const f
  * 2^(s - 127); the weight is e4m3(code) * 2^(s - 127).
  *   w_gate, w_up [E,I,H] and w_down [E,H,I]: E4M3 codes, one byte each, the layout of the
  *            bf16 weights of beam_moe_forward (16-byte aligned)
- *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes (16-byte aligned),
- *            s in 1..254, chosen so that every decoded weight is a normal bf16 number (or zero)
- * Every other argument, the workspace and the results are as for beam_moe_forward.  The
- * weights are decoded to bf16 exactly (an E4M3 value times a power of two is a bf16
- * value) and the layer then computes exactly what beam_moe_forward computes on the
- * decoded weights; only the weight bytes read from memory halve.  This storage format is
+ *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes (16-byte aligned):
+ *            2^(s - 127) for s = 0 .. 254 (s = 0 is 2^-127) and NaN for s = 255, as the
+ *            E8M0 format defines them
+ * Every other argument, the workspace and the results are as for beam_moe_forward.  A
+ * weight whose decoded value is a normal bf16 number (or zero) is decoded exactly (an E4M3
+ * value times a power of two is then a bf16 value) and the layer computes exactly what
+ * beam_moe_forward computes on the decoded weights; only the weight bytes read from memory
+ * halve.  Decoded values beyond that range are rounded to bf16 (to nearest, ties to even:
+ * below 2^-126 to a subnormal or zero, above the largest bf16 to infinity); a NaN code or a
+ * NaN scale makes the outputs of the tokens routed to that expert NaN.  This storage format is
  * not on the Beam pages (they quote FP8 checkpoints without a scale scheme); it is the
  * block-scaled layout of the OCP microscaling formats with 32-element blocks.
  */
@@ -216,12 +220,14 @@ beam_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, con
  * share one E8M0 scale byte s, meaning 2^(s - 127); the weight is e2m1(code) * 2^(s - 127).
  *   w_gate, w_up [E,I,H/2] and w_down [E,H,I/2]: packed E2M1 codes, the rows of the bf16
  *            weights of beam_moe_forward at half a byte per element (16-byte aligned)
- *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes (16-byte aligned),
- *            s in 1..254, chosen so that every decoded weight is a normal bf16 number (or zero)
- * Every other argument, the workspace and the results are as for beam_moe_forward.  The
- * weights are decoded to bf16 exactly and the layer then computes exactly what
- * beam_moe_forward computes on the decoded weights; the weight bytes read from memory are
- * a quarter (plus 1/32 byte of scale per weight).  The pages quote a ~4.5-bit checkpoint
+ *   s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]: E8M0 scale bytes (16-byte aligned):
+ *            2^(s - 127) for s = 0 .. 254 and NaN for s = 255, as for beam_moe_forward_fp8
+ * Every other argument, the workspace and the results are as for beam_moe_forward.  A
+ * weight whose decoded value is a normal bf16 number (or zero) is decoded exactly and the
+ * layer computes exactly what beam_moe_forward computes on the decoded weights; the weight
+ * bytes read from memory are a quarter (plus 1/32 byte of scale per weight).  Decoded
+ * values beyond that range are rounded to bf16 as for beam_moe_forward_fp8; a NaN scale
+ * makes the outputs of the tokens routed to that expert NaN.  The pages quote a ~4.5-bit checkpoint
  * format for another GPU family without its layout; this is the OCP microscaling MXFP4
  * format, the 4-bit format of this GPU's matrix cores.
  */
