@@ -238,6 +238,28 @@ beam_status beam_moe_forward_mxfp4(const beam_moe_shape* shape, const void* x, c
                                    float* topk_w, void* moe_y, void* ws, size_t ws_bytes, void* const* stage_events,
                                    void* stream);
 
+/*
+ * beam_moe_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a static device array of BEAM_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends (no allocation per call; the
+ * array's address is looked up once per device, on the first call there).
+ *   Arguments and results: as beam_moe_forward, minus ws / ws_bytes.  stream must belong to
+ *   the current device (else BEAM_ERR_INVALID_ARG).
+ *   Limit: shapes whose beam_moe_workspace_size (BEAM_OP_FORWARD, or
+ *   BEAM_OP_FORWARD_SUBLAYER with sub) exceeds BEAM_NOALLOC_SCRATCH_BYTES are rejected with
+ *   BEAM_ERR_WORKSPACE before any launch (T <= 768 tokens at the Beam layer's shape,
+ *   H = 5120, I = 2560, E = 256, top-8; use beam_moe_forward beyond).
+ *   Calls on one GPU share its array: calls that overlap on one GPU (different streams, or
+ *   different host threads) race and give wrong results; serialize them.
+ * Its results are those of beam_moe_forward on the same arguments (same kernels).
+ */
+#define BEAM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+beam_status beam_moe_forward_noalloc(const beam_moe_shape* shape, const void* x, const float* w_router,
+                                     const float* bias, const void* w_gate, const void* w_up, const void* w_down,
+                                     const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w,
+                                     void* moe_y, void* const* stage_events, void* stream);
+
 /* Static description of a status code. */
 const char* beam_status_string(beam_status status);
 

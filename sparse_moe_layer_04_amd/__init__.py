@@ -34,7 +34,8 @@ STAGE_NAMES = ("prenorm", "router_logits", "router_select", "permute", "gate_up"
 
 # exported C symbols (declared in include/beam_moe.h)
 EXPORTS = ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward",
-           "beam_moe_forward_fp8", "beam_moe_forward_mxfp4", "beam_status_string", "beam_moe_abi_version")
+           "beam_moe_forward_fp8", "beam_moe_forward_mxfp4", "beam_moe_forward_noalloc", "beam_status_string",
+           "beam_moe_abi_version")
 
 
 class Shape(ctypes.Structure):
@@ -58,8 +59,11 @@ _lib.beam_moe_forward.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp
 _lib.beam_moe_forward_fp8.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.POINTER(Sublayer), _vp, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp]
 _lib.beam_moe_forward_mxfp4.argtypes = _lib.beam_moe_forward_fp8.argtypes
+_lib.beam_moe_forward_noalloc.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.POINTER(Sublayer), _vp, _vp, _vp, _vp, ctypes.POINTER(_vp), _vp]
+NOALLOC_SCRATCH_BYTES = 128 << 20   # BEAM_NOALLOC_SCRATCH_BYTES
 for _f in ("beam_moe_workspace_size", "beam_moe_rmsnorm", "beam_moe_route", "beam_moe_permute", "beam_moe_forward",
-           "beam_moe_forward_fp8", "beam_moe_forward_mxfp4"):
+           "beam_moe_forward_fp8", "beam_moe_forward_mxfp4", "beam_moe_forward_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.beam_status_string.argtypes = [ctypes.c_int]
 _lib.beam_status_string.restype = ctypes.c_char_p
@@ -166,6 +170,22 @@ def forward(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, out, ws, subl
                                    _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd), sub, _ptr(out),
                                    _ptr(topk_idx), _ptr(topk_w), _ptr(moe_y), _ptr(ws), _nbytes(ws), ev,
                                    _stream(stream)), name)
+
+
+def forward_noalloc(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, out, sublayer: Optional[Sublayer] = None,
+                    topk_idx=None, topk_w=None, moe_y=None, stage_events: Optional[Sequence[int]] = None,
+                    stream=None):
+    """beam_moe_forward_noalloc: beam_moe_forward with the library's static device scratch
+    instead of a workspace (no allocation; calls overlapping on one GPU race)."""
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != NUM_STAGES + 1:
+            raise ValueError("need %d stage events" % (NUM_STAGES + 1))
+        ev = (_vp * (NUM_STAGES + 1))(*stage_events)
+    sub = ctypes.byref(sublayer) if sublayer is not None else None
+    _check(_lib.beam_moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+                                         _ptr(w_up), _ptr(w_down), sub, _ptr(out), _ptr(topk_idx), _ptr(topk_w),
+                                         _ptr(moe_y), ev, _stream(stream)), "beam_moe_forward_noalloc")
 
 
 def sublayer(pre_gain, post_gain, eps: float, residual_k: float) -> Sublayer:

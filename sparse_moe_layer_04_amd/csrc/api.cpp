@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace {
@@ -293,6 +295,65 @@ beam_status beam_moe_forward_mxfp4(const beam_moe_shape* shape, const void* x, c
     const WeightScales sc{s_gate, s_up, s_down, beam::WF_E2M1};
     return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, &sc, sub, out, topk_idx, topk_w, moe_y, ws,
                         ws_bytes, stage_events, stream);
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward ------------------------------------------------------------
+//
+// The workspace of beam_moe_forward_noalloc: a file-scope device array (each GPU that loads
+// the library holds its own copy until the process ends).  In host code `scratch` is only a
+// stand-in for the symbol; its device address on a GPU comes from hipGetSymbolAddress with
+// that GPU current, looked up on the entry point's first call on the GPU and kept per device.
+// Nothing in the array has to start at zero: every region of the forward workspace is
+// written before it is read within a call.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[BEAM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];   // device address of `scratch` per device, nullptr until looked up
+
+// the scratch array's address on the device of `stream` (which must be the current device)
+beam_status device_scratch(void* stream, void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BEAM_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return BEAM_ERR_HIP;
+        if (sdev != dev) return BEAM_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_moe_forward_noalloc(const beam_moe_shape* shape, const void* x, const float* w_router,
+                                     const float* bias, const void* w_gate, const void* w_up, const void* w_down,
+                                     const beam_sublayer* sub, void* out, int32_t* topk_idx, float* topk_w,
+                                     void* moe_y, void* const* stage_events, void* stream) {
+    if (!shape_valid(shape)) return BEAM_ERR_INVALID_ARG;
+    if (!shape_supported(shape)) return BEAM_ERR_UNSUPPORTED;
+    if (shape->T == 0)   // no launch, no scratch: argument checks as beam_moe_forward
+        return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, nullptr, sub, out, topk_idx, topk_w,
+                            moe_y, nullptr, 0, stage_events, stream);
+    if (make_layout(shape, sub ? BEAM_OP_FORWARD_SUBLAYER : BEAM_OP_FORWARD).total > BEAM_NOALLOC_SCRATCH_BYTES)
+        return BEAM_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const beam_status st = device_scratch(stream, &ws);
+    if (st != BEAM_OK) return st;
+    return forward_impl(shape, x, w_router, bias, w_gate, w_up, w_down, nullptr, sub, out, topk_idx, topk_w, moe_y,
+                        ws, BEAM_NOALLOC_SCRATCH_BYTES, stage_events, stream);
 }
 
 }  // extern "C"
