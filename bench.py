@@ -180,6 +180,29 @@ def ingest_counters(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write
     print(json.dumps({workload: ent}))
 
 
+def trace_summary(csv_path, skip):
+    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace csv, leaving out
+    the first `skip` dispatches of every kernel (the untimed warm-up steps of a one-workload
+    bench run), so the means cover the same forwards as the bench's timing."""
+    import csv
+    durs = {}
+    for r in csv.DictReader(open(csv_path)):
+        durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = []
+    for name, d in durs.items():
+        d = d[skip:] if len(d) > skip else d
+        rows.append((name, len(d), sum(d) / len(d), statistics.median(d), min(d), max(d)))
+    total = sum(r[1] * r[2] for r in rows)
+    rows.sort(key=lambda r: -r[1] * r[2])
+    out = ["| kernel | dispatches | mean (us) | median (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|---|"]
+    for name, n, mean, med, lo, hi in rows:
+        short = name.split("(")[0]
+        out.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% |" % (short, n, mean, med, lo, hi,
+                                                                          100.0 * n * mean / total))
+    return "\n".join(out)
+
+
 def expert_histogram(counts):
     """The per-expert routed-row counts of a step: touched, min, median, max, empty, top-8."""
     import numpy as np
@@ -417,10 +440,16 @@ def main():
                          "and print one JSON line per size instead of the benchmark line")
     ap.add_argument("--sweep-md", default="", metavar="PATH", help="also write the sweep as a markdown table")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "SKIP"),
+                    help="print the per-kernel duration table of a rocprofv3 kernel trace, leaving out the "
+                         "first SKIP dispatches of each kernel (no GPU needed)")
     ap.add_argument("--ingest-pmc", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV",
                                                       "CALIB_MIB"),
                     help="record counter runs of --workload into profiles/traffic.json (no GPU needed)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary[0], int(args.trace_summary[1])))
+        return
     if args.ingest_pmc:
         a = args.ingest_pmc
         ingest_counters(args.workload, a[0], a[1], a[2], a[3], int(a[4]))

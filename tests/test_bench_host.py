@@ -112,3 +112,19 @@ def test_layer_work_counts_touched_experts_router_and_activations():
     tiny = CONFIGS["tiny_f32"]
     f, b = bench.layer_work(tiny, 16)
     assert b == 16 * 3.0 * 64 * 32 * 4 + 16 * 64 * 4 + 2 * 32 * 64 * 4     # fp32 weights and activations
+
+
+def test_trace_summary_leaves_out_the_warm_up_dispatches(tmp_path):
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i, us in enumerate([50, 40, 10, 10, 12]):      # two warm-ups, then three timed
+            w.writerow({"Kernel_Name": "void beam::k<true>(int)", "Start_Timestamp": 1000 * i,
+                        "End_Timestamp": 1000 * i + us * 1000})
+        w.writerow({"Kernel_Name": "other(int)", "Start_Timestamp": 0, "End_Timestamp": 5000})
+    table = bench.trace_summary(str(path), 2)
+    line = [l for l in table.splitlines() if "beam::k<true>" in l][0]
+    cells = [c.strip() for c in line.split("|")]
+    assert cells[2] == "3" and cells[3] == "10.7" and cells[4] == "10.0" and cells[5] == "10.0" and cells[6] == "12.0"
+    assert "other" in table      # a kernel with fewer dispatches than the skip keeps them all
