@@ -680,23 +680,28 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
                                    : (int64_t)(c.row_begin + src);
         avoff[i] = (uint32_t)((r * c.K + ch * 8) * 2);
     }
+    // bf16: k-chunk c of a row is kept at position 2c (c < 4) or 2(c-4)+1 of its LDS row, so
+    // the fragments of k-chunks g and 4+g (the lane's weight chunks, below) are read from
+    // positions 2g and 2g+1: the read pattern the XOR layout keeps free of bank conflicts
+    // (reading positions g and 4+g conflicted in 28% of the LDS cycles)
+    auto kpos = [&](int ch) { return WF == WF_BF16 ? (ch < 4 ? 2 * ch : 2 * ch - 7) : ch; };
     auto lds_slot = [&](int i) {
         const int q = (tid + i * THREADS) % ACH;
-        return w_off(q >> 3, q & 7);
+        return w_off(q >> 3, kpos(q & 7));
     };
     u32x4 sa[AL];
     auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
     auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
     auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
     auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, WF>(c, rb, rs, b, kstep, set); };
-    // fragment read offsets: row r*16 + (lane & 15), chunks 2g and 2g+1 (g = lane >> 4)
+    // fragment read offsets: row r*16 + (lane & 15), LDS positions 2g and 2g+1 (g = lane >> 4).
+    // bf16 weights: the even MFMA takes k-chunk g of the step's 128 bytes, the odd one k-chunk
+    // 4+g (each weight load then reads 64 contiguous bytes of 16 rows: one 64-byte request per
+    // row), which kpos puts at positions 2g and 2g+1; the 8-bit and 4-bit codes of a lane's 16
+    // elements are contiguous, so there the two MFMAs take k-chunks 2g and 2g+1 themselves
     const int fr = lane & 15, g = lane >> 4;
-    // bf16 weights: the even MFMA takes chunk g of the step's 128 bytes, the odd one chunk 4+g
-    // (each weight load then reads 64 contiguous bytes of 16 rows: one 64-byte request per
-    // row); the 8-bit and 4-bit codes of a lane's 16 elements are contiguous, so there the
-    // two MFMAs take chunks 2g and 2g+1
-    const int off_e = w_off(fr, WF == WF_BF16 ? g : 2 * g);
-    const int off_o = w_off(fr, WF == WF_BF16 ? 4 + g : 2 * g + 1);
+    const int off_e = w_off(fr, 2 * g);
+    const int off_o = w_off(fr, 2 * g + 1);
     constexpr int LA = 1;  // fragment lookahead (row blocks); deeper measured no faster
 
     // memory operations of a step, in issue order: with weights one step ahead (RING = 2)
