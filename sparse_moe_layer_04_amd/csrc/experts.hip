@@ -17,8 +17,19 @@
 #include "common.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace beam {
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 // ---------------------------------------------------------------------------------
 // bf16 grouped GEMM on MFMA (16x16x32, fp32 accumulation).
@@ -357,7 +368,10 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         if constexpr (SW == 128) {   // one block per lane and step: byte 4j + g
             return e8m0_factor((sc[blk][j] >> (8 * (lane >> 4))) & 0xFFu);
         } else {                     // two: bytes 8j + 2g + h
-            const uint32_t d = (lane & 32) ? sc[blk][2 * j + 1] : sc[blk][2 * j];
+            // lanes 32..63 take the odd word (a bit select: a conditional pick of the two
+            // array elements becomes a load at a lane-dependent index from a private array)
+            const uint32_t lo = sc[blk][2 * j], hi = sc[blk][2 * j + 1];
+            const uint32_t d = lo ^ ((lo ^ hi) & (0u - (uint32_t)((lane >> 5) & 1)));
             return e8m0_factor((d >> (8 * (2 * ((lane >> 4) & 1) + h))) & 0xFFu);
         }
     };
@@ -400,7 +414,8 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
         }
     };
     // prologue: chunk 0 into LDS, chunk 1 in flight, weights RING-1 steps ahead (issuing the
-    // weights before the activation lookups measured no faster)
+    // weights before the scale rows and the activation lookups measured no faster: 8-bit
+    // down 2% slower, the others within 0.6%)
     stage_s_load();
     __builtin_amdgcn_sched_barrier(0);
     load_a(0);
@@ -801,9 +816,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     __builtin_amdgcn_sched_barrier(0);
     int kt = 0;
     for (; kt + UNR <= nk; kt += UNR) {
-        [&]<int... J>(std::integer_sequence<int, J...>) {
-            (step(kt + J, std::integral_constant<int, J>()), ...);
-        }(std::make_integer_sequence<int, UNR>());
+        static_for<UNR>([&](auto jc) { step(kt + decltype(jc)::value, jc); });
     }
     // remainder: nk is even and nk - kt < UNR <= 6
     if (nk - kt >= 2) {

@@ -189,6 +189,16 @@ MID_CASES = {
                                            weights="mxfp4", seed_base=38000),
     "mid_h1024_t257": mid_config("mid_h1024_t257", 257, H=1024, I=384, E=32, n_group=4, topk_group=2, top_k=6,
                                  wr_std=math.sqrt(1.0 / 1024), seed_base=16000),
+    # many decode work items (1400-1500 gate/up and 700-750 down: ~93 touched experts of
+    # 128, 16 and 8 column blocks), more than two work-groups per CU hold at once; the mild
+    # skew puts tiles of 1, 2 and up to 4 row blocks (and in the bf16 case one larger tile)
+    # among them; K = 1024 gives the 16-row stream two activation chunks; all three formats
+    "mid_items_e128_t96": mid_config("mid_items_e128_t96", 96, H=1024, I=1024, E=128, bias="zipf:0.12",
+                                     wr_std=math.sqrt(1.0 / 1024), seed_base=42000),
+    "mid_fp8_items_e128_t96": mid_config("mid_fp8_items_e128_t96", 96, H=1024, I=1024, E=128, bias="zipf:0.12",
+                                         weights="fp8", wr_std=math.sqrt(1.0 / 1024), seed_base=43000),
+    "mid_mxfp4_items_e128_t96": mid_config("mid_mxfp4_items_e128_t96", 96, H=1024, I=1024, E=128, bias="zipf:0.12",
+                                           weights="mxfp4", wr_std=math.sqrt(1.0 / 1024), seed_base=44000),
 }
 
 
