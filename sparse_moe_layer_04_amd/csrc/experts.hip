@@ -622,6 +622,22 @@ __device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t vof
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+// bf16 rows keep k-chunk c at position kpos(c) = 2c (c < 4) or 2(c-4)+1 of their LDS row (then
+// XOR-swizzled by w_swz); kinv is its inverse: the chunk kept at position q
+__device__ __forceinline__ int kinv(int q) { return (q & 1) ? 4 + (q >> 1) : q >> 1; }
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at dst + 16 l
+__device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
+// Work-group barrier for LDS written by ds_write only: this wave's LDS writes are complete
+// (lgkmcnt), then s_barrier; the memory clobber keeps the compiler from moving LDS accesses
+// across it.  Unlike a release fence it does not wait for loads into LDS still in flight
+// (the fence turns into vmcnt(0) while any is outstanding), so the weight loads of the next
+// step keep flying across it.
+__device__ __forceinline__ void lds_write_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 
 struct LineCtx {
     __amdgpu_buffer_rsrc_t act;   // activation tensor (token rows or h rows)
@@ -630,6 +646,7 @@ struct LineCtx {
     __amdgpu_buffer_rsrc_t s0;    // quantized weights: scale rows of the blocks of w0
     __amdgpu_buffer_rsrc_t s1;    //       and of w1
     uint32_t wvoff;               // this lane's byte offset inside a weight block
+    uint32_t wdoff[2];            // bf16: this lane's byte offsets for the two 8-row loads into LDS
     uint32_t svoff;               // quantized weights: this lane's byte offset inside a block's scale rows
     int K, top_k, row_begin, row_count;
     bool gather;
@@ -642,40 +659,46 @@ struct LineCtx {
 // E2M1 one 8-byte load, and the scale byte of their 32-k block.
 template <int NB, int RING, int WF>
 __device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB],
-                                            int b, int kstep, int set) {
+                                            uint16_t* const (&wl)[2], int b, int kstep, int set) {
     constexpr int HB = NB / 2;
     constexpr int WB = wbits(WF);
     const int nk = c.K / WKS;
     const int ks = kstep < nk ? kstep : nk - 1;
     const uint32_t so = (uint32_t)(ks * WKS * WB / 8) + (uint32_t)(b % HB) * (uint32_t)(16 * c.K * WB / 8);
     const __amdgpu_buffer_rsrc_t r = b < HB ? c.w0 : c.w1;
+    if constexpr (WF == WF_BF16) {
+        // whole 128-byte lines of 8 rows per load, into the wave's block b of LDS slot `set`
+        (void)rb;
+        uint16_t* dst = wl[set] + b * 16 * WKS;
+        buf_load_lds(r, dst, c.wdoff[0], so);
+        buf_load_lds(r, dst + 8 * WKS, c.wdoff[1], so);
+        return;
+    }
     if constexpr (WF == WF_E2M1) {
         const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, c.wvoff, so, 0));
         rb[set][b][0] = u32x4{v.x, v.y, 0u, 0u};
     } else {
         rb[set][b][0] = buf_load(r, c.wvoff, so);
     }
-    if constexpr (WF != WF_BF16) {
-        const uint32_t ss = (uint32_t)(ks * (WKS / 32)) + (uint32_t)(b % HB) * (uint32_t)(16 * (c.K / 32));
-        rs[set][b] = __builtin_amdgcn_raw_buffer_load_b8(b < HB ? c.s0 : c.s1, c.svoff, ss, 0);
-    } else {
-        rb[set][b][1] = buf_load(r, c.wvoff + 64, so);
-    }
+    const uint32_t ss = (uint32_t)(ks * (WKS / 32)) + (uint32_t)(b % HB) * (uint32_t)(16 * (c.K / 32));
+    rs[set][b] = __builtin_amdgcn_raw_buffer_load_b8(b < HB ? c.s0 : c.s1, c.svoff, ss, 0);
 }
 
 // The weights of a work item's first RING-1 steps.
 template <int NB, int RING, int WF>
-__device__ __forceinline__ void line_prologue_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB]) {
+__device__ __forceinline__ void line_prologue_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB],
+                                                uint16_t* const (&wl)[2]) {
 #pragma unroll
     for (int s2 = 0; s2 < RING - 1; ++s2)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) line_load_b<NB, RING, WF>(c, rb, rs, b, s2, s2);
+        for (int b = 0; b < NB; ++b) line_load_b<NB, RING, WF>(c, rb, rs, wl, b, s2, s2);
 }
 
 // Main loop of one work item; the caller has issued its first RING-1 weight steps.
 template <int WAVES, int NB, int RING, int NRB, int WF>
 __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4 (&rb)[RING][NB][2],
-                                          uint32_t (&rs)[RING][NB], f32x4 (&acc)[NRB][NB]) {
+                                          uint32_t (&rs)[RING][NB], uint16_t* const (&wl)[2],
+                                          f32x4 (&acc)[NRB][NB]) {
     constexpr int THREADS = WAVES * 64;
     constexpr int ACH = NRB * 16 * 8;                  // 16-byte activation chunks per step
     constexpr int AL = (ACH + THREADS - 1) / THREADS;
@@ -708,7 +731,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
     auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
     auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
-    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, WF>(c, rb, rs, b, kstep, set); };
+    auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, WF>(c, rb, rs, wl, b, kstep, set); };
     // fragment read offsets: row r*16 + (lane & 15), LDS positions 2g and 2g+1 (g = lane >> 4).
     // bf16 weights: the even MFMA takes k-chunk g of the step's 128 bytes, the odd one k-chunk
     // 4+g (each weight load then reads 64 contiguous bytes of 16 rows: one 64-byte request per
@@ -747,7 +770,10 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
         constexpr int nset = (j + RING - 1) % RING;     // ring slot of step kt+RING-1
         const uint16_t* L = lds + (j & 1) * WBUF_ELEMS;
         const int wbuf = (j + 1) & 1;
-        lds_barrier();
+        if constexpr (WF == WF_BF16)
+            lds_write_barrier();   // bf16 weights of the next step are loading into LDS
+        else
+            lds_barrier();
         // this step's weight fragments (quantized weights: decoded exactly to bf16)
         bf16x8 wf[NB][2];
 #pragma unroll
@@ -760,9 +786,9 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
                 const float sc = e8m0_factor(rs[set][b]);
                 wf[b][0] = decode8_fp4(rb[set][b][0][0], sc);
                 wf[b][1] = decode8_fp4(rb[set][b][0][1], sc);
-            } else {
-                wf[b][0] = __builtin_bit_cast(bf16x8, rb[set][b][0]);
-                wf[b][1] = __builtin_bit_cast(bf16x8, rb[set][b][1]);
+            } else {   // bf16: this wave's rows of LDS slot `set`, read like the activations
+                wf[b][0] = *(const bf16x8*)(wl[set] + b * 16 * WKS + off_e);
+                wf[b][1] = *(const bf16x8*)(wl[set] + b * 16 * WKS + off_o);
             }
         }
         bf16x8 ae[NRB], ao[NRB];
@@ -771,7 +797,8 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
             ae[r] = *(const bf16x8*)(L + off_e + r * 16 * WKS);
             ao[r] = *(const bf16x8*)(L + off_o + r * 16 * WKS);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+        // (bf16: the weight fragments are LDS reads too)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA + (WF == WF_BF16 ? 2 * NB : 0), 0);
 #pragma unroll
         for (int r = 0; r < NRB; ++r) {
             if (r + LA < NRB) {
@@ -836,11 +863,19 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     int top_k, const int32_t* __restrict__ sorted_pairs, const TileEntry* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_col_blocks, uint16_t* __restrict__ C) {
     static_assert(WAVES * NB * 16 == 256 && NB % 2 == 0, "a work-group covers 256 weight rows");
-    // the output tile is staged through LDS (rows padded by 16 bytes) once the main loop is done
+    // the output tile is staged through LDS (rows padded by 16 bytes) once the main loop is
+    // done, EPI_RB row blocks at a time (bf16 down: half the tile, so that with the bf16
+    // weight slots below everything fits in 160 KB)
     constexpr int EPI_COLS = GATED ? WAVES * (NB / 2) * 16 : WAVES * NB * 16;
     constexpr int EPI_STRIDE = EPI_COLS + 8;
-    constexpr int LDS_ELEMS = GROWS * EPI_STRIDE > 2 * WBUF_ELEMS ? GROWS * EPI_STRIDE : 2 * WBUF_ELEMS;
+    constexpr int EPI_RB = GATED || WF != WF_BF16 ? GROWS / 16 : GROWS / 32;
+    constexpr int LDS_ELEMS = EPI_RB * 16 * EPI_STRIDE > 2 * WBUF_ELEMS ? EPI_RB * 16 * EPI_STRIDE : 2 * WBUF_ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+    // bf16 weights: two slots (steps of even and odd parity), each wave's 16*NB rows x 128
+    // bytes; two arrays, so that a read of one slot waits only for the loads into that slot
+    constexpr int WSLOT = WF == WF_BF16 ? WAVES * NB * 16 * WKS : 8;
+    __shared__ __attribute__((aligned(16))) uint16_t wlds0[WSLOT];
+    __shared__ __attribute__((aligned(16))) uint16_t wlds1[WSLOT];
     constexpr int HB = NB / 2;
 
     // XCD-aware order (blocks are dealt to the 8 XCDs round-robin): each XCD takes a
@@ -876,6 +911,14 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     c.wvoff = (uint32_t)(WF == WF_BF16 ? ((lane & 15) * K * 2 + (lane >> 4) * 16)
                                        : ((lane & 15) * K + (lane >> 4) * 16) * WB / 8);
     c.svoff = (uint32_t)((lane & 15) * (K / 32) + (lane >> 5));   // scale block of elements 16*(lane>>4)
+    // bf16 weights into LDS: load i covers block rows 8i .. 8i+7, lane l lands at position l&7
+    // of row 8i + (l>>3) and so loads the k-chunk kept there (the activations' layout)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * i + (lane >> 3);
+        c.wdoff[i] = (uint32_t)(row * K * 2 + kinv((lane & 7) ^ w_swz(row)) * 16);
+    }
+    uint16_t* const wl[2] = {wlds0 + wave * (NB * 16 * WKS), wlds1 + wave * (NB * 16 * WKS)};
     const uint32_t bytes = (uint32_t)((int64_t)HB * 16 * K * WB / 8);
     const uint32_t sbytes = (uint32_t)(HB * 16 * (K / 32));
     int col0;
@@ -901,47 +944,52 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
         constexpr int NRB = decltype(nrbc)::value;
         u32x4 rb[RING][NB][2];
         uint32_t rs[RING][NB];
-        line_prologue_b<NB, RING, WF>(c, rb, rs);
+        line_prologue_b<NB, RING, WF>(c, rb, rs, wl);
         f32x4 acc[NRB][NB];
 #pragma unroll
         for (int r = 0; r < NRB; ++r)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        line_body<WAVES, NB, RING, NRB, WF>(c, lds, rb, rs, acc);
+        line_body<WAVES, NB, RING, NRB, WF>(c, lds, rb, rs, wl, acc);
         // epilogue: each wave writes its bf16 columns of the tile into LDS (C layout of a
         // 16x16 block: rows 4*(lane>>4)+q, column lane&15), then the work-group stores
-        // whole 16-byte chunks of every output row.  silu(g) = g / (1 + e^-g) with the
-        // hardware reciprocal (the result is rounded to bf16).
-        lds_barrier();  // every wave is done with the activation buffers
+        // whole 16-byte chunks of every output row; EPI_RB row blocks at a time.
+        // silu(g) = g / (1 + e^-g) with the hardware reciprocal (the result is rounded to bf16).
         const int wcol = col0 - cblk * EPI_COLS;
+        static_for<(NRB + EPI_RB - 1) / EPI_RB>([&](auto hc) {
+            constexpr int R0 = decltype(hc)::value * EPI_RB;
+            constexpr int RN = NRB - R0 < EPI_RB ? NRB - R0 : EPI_RB;   // row blocks of this part
+            lds_barrier();  // every wave is done with the LDS it overwrites
 #pragma unroll
-        for (int r = 0; r < NRB; ++r)
+            for (int r = 0; r < RN; ++r)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint16_t* lrow = lds + (r * 16 + 4 * (lane >> 4) + q) * EPI_STRIDE + wcol + (lane & 15);
-                if (GATED) {
+                for (int q = 0; q < 4; ++q) {
+                    uint16_t* lrow = lds + (r * 16 + 4 * (lane >> 4) + q) * EPI_STRIDE + wcol + (lane & 15);
+                    if (GATED) {
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        const float gv = acc[r][hb][q], uv = acc[r][HB + hb][q];
-                        lrow[16 * hb] = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+                        for (int hb = 0; hb < HB; ++hb) {
+                            const float gv = acc[R0 + r][hb][q], uv = acc[R0 + r][HB + hb][q];
+                            lrow[16 * hb] = f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+                        }
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) lrow[16 * b] = f32_to_bf16(acc[R0 + r][b][q]);
                     }
-                } else {
+                }
+            lds_barrier();
+            constexpr int CPR = EPI_COLS / 8;  // 16-byte chunks per output row
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) lrow[16 * b] = f32_to_bf16(acc[r][b][q]);
+            for (int q0 = 0; q0 < RN * 16 * CPR; q0 += WAVES * 64) {
+                const int q = q0 + (int)threadIdx.x;
+                const int row = q / CPR, ch = q % CPR;
+                if (q < RN * 16 * CPR && R0 * 16 + row < c.row_count) {
+                    const u32x4 v = *(const u32x4*)(lds + row * EPI_STRIDE + ch * 8);
+                    const int trow = c.row_begin + R0 * 16 + row;
+                    const int64_t orow = GATED ? (int64_t)trow : (int64_t)c.sorted_pairs[trow];
+                    *(u32x4*)(C + orow * N + cblk * EPI_COLS + ch * 8) = v;
                 }
             }
-        lds_barrier();
-        constexpr int CPR = EPI_COLS / 8;  // 16-byte chunks per output row
-#pragma unroll
-        for (int q0 = 0; q0 < NRB * 16 * CPR; q0 += WAVES * 64) {
-            const int q = q0 + (int)threadIdx.x;
-            const int row = q / CPR, ch = q % CPR;
-            if (q < NRB * 16 * CPR && row < c.row_count) {
-                const u32x4 v = *(const u32x4*)(lds + row * EPI_STRIDE + ch * 8);
-                const int64_t orow = GATED ? (int64_t)(c.row_begin + row) : (int64_t)c.sorted_pairs[c.row_begin + row];
-                *(u32x4*)(C + orow * N + cblk * EPI_COLS + ch * 8) = v;
-            }
-        }
+        });
     };
     // row-block variants: 13..18 cover prefill-sized experts without padding blocks
     const int nrb = (te.row_count + 15) >> 4;
