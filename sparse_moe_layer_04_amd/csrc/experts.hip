@@ -591,16 +591,18 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
 // of WAVES waves gives each wave NB 16-row weight blocks (gate/up: NB/2 gate blocks and
 // the up blocks of the same h columns).
 //
-// K advances 64 per step.  Weights: for each block a lane loads two 16-byte chunks of its
-// row's 128-byte window (bf16: chunks g and 4+g, g = lane>>4, so each load reads 64
-// contiguous bytes of 16 rows; codes: the lane's 16 contiguous elements), so every block
-// reads whole cache lines each step; the even MFMA of a step takes the first chunk, the odd
-// MFMA the second, and the activation fragments use the same k order.  Weight loads
-// run RING-1 steps ahead in a ring of RING register sets.  Activations: the rows of
-// step kt+1 are written into one of two LDS buffers while step kt is multiplied out of
-// the other, and one barrier per step publishes them.  The LDS writes and every global
-// load of a step are spread over its MFMA sequence.  Buffer loads with 32-bit offsets
-// keep one address register per weight stream.
+// K advances 64 per step.  bf16 weights go straight into LDS, whole 128-byte lines of 8
+// rows per load (16 bytes per lane), one step ahead, into two slots; each wave reads its
+// own rows back as MFMA fragments.  (Loaded into registers in the MFMA operand shape, 16
+// rows per load, they would be read as 64-byte half lines, which cost 11% more on the load
+// path once the activation stream shares it.)  The even MFMA of a step takes k-chunk g of
+// a row (g = lane>>4), the odd one 4+g, and the activation fragments use the same k order.
+// 8-bit and 4-bit codes: the lane's 16 contiguous elements per block and step, loaded into
+// a ring of RING register sets, RING-1 steps ahead, with their scale byte.  Activations:
+// the rows of step kt+1 are written into one of two LDS buffers while step kt is
+// multiplied out of the other, and one barrier per step publishes them.  The LDS writes
+// and every global load of a step are spread over its MFMA sequence.  Buffer loads with
+// 32-bit offsets keep one address register per stream.
 // ---------------------------------------------------------------------------------
 constexpr int WKS = 64;                    // k per step
 constexpr int WBUF_ELEMS = GROWS * WKS;    // one LDS activation buffer (36 KB)
@@ -645,7 +647,7 @@ struct LineCtx {
     __amdgpu_buffer_rsrc_t w1;    // weight blocks [NB/2, NB)
     __amdgpu_buffer_rsrc_t s0;    // quantized weights: scale rows of the blocks of w0
     __amdgpu_buffer_rsrc_t s1;    //       and of w1
-    uint32_t wvoff;               // this lane's byte offset inside a weight block
+    uint32_t wvoff;               // codes: this lane's byte offset inside a weight block
     uint32_t wdoff[2];            // bf16: this lane's byte offsets for the two 8-row loads into LDS
     uint32_t svoff;               // quantized weights: this lane's byte offset inside a block's scale rows
     int K, top_k, row_begin, row_count;
@@ -653,10 +655,11 @@ struct LineCtx {
     const int32_t* sorted_pairs;
 };
 
-// Weight loads of step `kstep` of a work item into ring slot `set` (steps past the end
-// reload the last step, which the cache still holds).  bf16: two 16-byte chunks per block
-// (a whole 128-byte line per row); E4M3: one 16-byte load of the same 16 elements per lane,
-// E2M1 one 8-byte load, and the scale byte of their 32-k block.
+// Weight loads of step `kstep` of a work item into slot `set` (steps past the end reload
+// the last step, which the cache still holds).  bf16: the block's 16 rows x 128 bytes into
+// the wave's LDS slot, two loads of 8 whole lines; E4M3: one 16-byte load of the lane's 16
+// elements into the register ring, E2M1 one 8-byte load, and the scale byte of their 32-k
+// block.
 template <int NB, int RING, int WF>
 __device__ __forceinline__ void line_load_b(const LineCtx& c, u32x4 (&rb)[RING][NB][2], uint32_t (&rs)[RING][NB],
                                             uint16_t* const (&wl)[2], int b, int kstep, int set) {
@@ -904,10 +907,8 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     c.gather = GATED;
     c.sorted_pairs = sorted_pairs;
     constexpr int WB = wbits(WF);   // bits per weight
-    // bf16: lane (row lane&15, g = lane>>4) loads the 16-byte chunks g and 4+g of its row's
-    // 128-byte step, so each load instruction reads 16 rows x 64 contiguous bytes (one full
-    // 64-byte request per row; chunks 2g and 2g+1 would need two half-used requests per row).
-    // Codes: the lane's 16 elements 16g .. 16g+15 (E4M3 16 bytes, E2M1 8 bytes).
+    // codes: the lane's 16 elements 16g .. 16g+15 of its row (g = lane>>4; E4M3 16 bytes,
+    // E2M1 8 bytes); the bf16 weights use wdoff (below)
     c.wvoff = (uint32_t)(WF == WF_BF16 ? ((lane & 15) * K * 2 + (lane >> 4) * 16)
                                        : ((lane & 15) * K + (lane >> 4) * 16) * WB / 8);
     c.svoff = (uint32_t)((lane & 15) * (K / 32) + (lane >> 5));   // scale block of elements 16*(lane>>4)
