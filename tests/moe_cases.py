@@ -199,6 +199,16 @@ MID_CASES = {
                                          weights="fp8", wr_std=math.sqrt(1.0 / 1024), seed_base=43000),
     "mid_mxfp4_items_e128_t96": mid_config("mid_mxfp4_items_e128_t96", 96, H=1024, I=1024, E=128, bias="zipf:0.12",
                                            weights="mxfp4", wr_std=math.sqrt(1.0 / 1024), seed_base=44000),
+    # the line kernel at K = 2560 (gate/up) and 1536 (down): 50 rows per expert, above every
+    # format's switch (bf16 8, 8-bit 40, 4-bit 44), 12 and 10 column blocks, 40 and 24 steps
+    "mid_line_h2560_t200": mid_config("mid_line_h2560_t200", 200, H=2560, I=1536, E=16, n_group=4, topk_group=2,
+                                      top_k=4, wr_std=math.sqrt(1.0 / 2560), seed_base=45000),
+    "mid_fp8_line_h2560_t200": mid_config("mid_fp8_line_h2560_t200", 200, H=2560, I=1536, E=16, n_group=4,
+                                          topk_group=2, top_k=4, weights="fp8", wr_std=math.sqrt(1.0 / 2560),
+                                          seed_base=46000),
+    "mid_mxfp4_line_h2560_t200": mid_config("mid_mxfp4_line_h2560_t200", 200, H=2560, I=1536, E=16, n_group=4,
+                                            topk_group=2, top_k=4, weights="mxfp4", wr_std=math.sqrt(1.0 / 2560),
+                                            seed_base=47000),
 }
 
 
