@@ -458,6 +458,32 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
 }
 
 // Runs one tile: main loop variant, then the epilogue.
+// Register sets of the stream variant's weight ring (weights run ring-1 steps ahead),
+// measured over decode and serving shapes (16..1280 tokens of the Beam layer): bf16 two steps
+// ahead (three were 1% slower); E4M3 one step ahead in 16-row tiles and two in larger ones
+// (three steps ahead was 4-5% slower from 64 to 512 tokens, 1.5-3% at 768-1024); E2M1 in
+// whole-line steps (16 MFMAs per block and step) one step ahead (two measured no faster,
+// three spill), in half-line steps three ahead (one or two were 1-4% slower).  A shallower
+// ring leaves fewer redundant loads of a row's last line when a work item ends, and issues
+// fewer loads at once when one starts.
+#ifndef STREAM_RING_BF16
+#define STREAM_RING_BF16 3
+#endif
+#ifndef STREAM_RING_E4M3_1
+#define STREAM_RING_E4M3_1 2
+#endif
+#ifndef STREAM_RING_E4M3_N
+#define STREAM_RING_E4M3_N 3
+#endif
+#ifndef STREAM_RING_E2M1_HALF
+#define STREAM_RING_E2M1_HALF 4
+#endif
+__host__ __device__ constexpr int stream_ring(int wf, int nrb) {
+    return wf == WF_E2M1 ? (stream_step_bytes(wf, nrb) == 128 ? 2 : STREAM_RING_E2M1_HALF)
+         : wf == WF_E4M3 ? (nrb == 1 ? STREAM_RING_E4M3_1 : STREAM_RING_E4M3_N)
+                         : STREAM_RING_BF16;
+}
+
 template <bool GATED, int WF, int NRB, int RING, int THREADS>
 __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
     const int lane = threadIdx.x & 63;
@@ -468,10 +494,7 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     constexpr int CHUNK = stream_chunk(NRB);
     if constexpr (NRB <= 4) {
         if (c.K % CHUNK == 0 && (WF == WF_BF16 || c.K <= SCALE_KMAX))
-            // E2M1 in whole-line steps (16 MFMAs per block and step): weights one step ahead
-            // (two steps ahead measured no faster; three spill)
-            tile_body_stream<GATED, WF, NRB, stream_step_bytes(WF, NRB) * 8 / wbits(WF) == 256 ? 2 : RING,
-                             THREADS>(c, &lds[0][0], acc);
+            tile_body_stream<GATED, WF, NRB, stream_ring(WF, NRB), THREADS>(c, &lds[0][0], acc);
         else
             tile_body<GATED, WF, NRB, RING, THREADS>(c, lds, acc);
     } else
