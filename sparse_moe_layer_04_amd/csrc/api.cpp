@@ -250,7 +250,7 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     }
     BEAM_TRY(mark(BEAM_STAGE_DOWN));
     if (bf16) {
-        BEAM_TRY(beam::launch_down(h, true, w_down, sc ? sc->format : beam::WF_BF16, sc ? sc->down : nullptr, P, H,
+        BEAM_TRY(beam::launch_down(h, true, w_down, sc ? sc->format : beam::WF_BF16, sc ? sc->down : nullptr, T, P, H,
                                    I, E, sorted, tiles, ntiles, L.max_tiles, L.tile_rows, ypair, s));
     } else {
         BEAM_TRY(beam::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w_down), H, I, sorted,

@@ -104,9 +104,10 @@ hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const 
                           const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                           int64_t max_tile_count, int tile_rows, void* h, hipStream_t s);
 
-// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T   (h: P rows; quantized weights with s_down)
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t P, int H,
-                       int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+// y_pair[sorted_pairs[row], :] = h[row, :] W_d^T   (h: P rows of the T tokens' routes; quantized
+// weights with s_down)
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t T,
+                       int64_t P, int H, int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s);
 
 // fp32 path (no tiles): one thread per output element

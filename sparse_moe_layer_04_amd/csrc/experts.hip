@@ -254,14 +254,15 @@ __host__ __device__ constexpr int stream_step_bytes(int wf, int nrb) {
 }
 constexpr int SACT_ELEMS = 2 * 16 * SKC;   // the double-buffered activation chunks
 constexpr int SCALE_KMAX = 8192;    // longest K whose scale rows fit the per-wave LDS area
-constexpr int SCALE_WAVE_BYTES = 2 * 16 * (SCALE_KMAX / 32);
+constexpr int SCALE_KMAX_SMALL = 5120;   // the same for the small-tile kernel
+__host__ __device__ constexpr int scale_wave_bytes(int kmax) { return 2 * 16 * (kmax / 32); }
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // LDS element offset of 16-byte chunk `ch` (0..C/8-1) of activation row `row` (C columns per row)
 template <int C>
 __device__ __forceinline__ int s_off(int row, int ch) { return row * C + ((ch ^ (row & 15)) << 3); }
 
-template <bool GATED, int WF, int NRB, int RING, int THREADS>
+template <bool GATED, int WF, int NRB, int RING, int THREADS, int SKMAX>
 __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds, f32x4 (&acc)[NRB][2]) {
     constexpr int ROWS = NRB * 16;
     constexpr int SKC = stream_chunk(NRB);
@@ -318,11 +319,11 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     // 8j + 2g and 8j + 2g + 1.  The wave's two blocks' scale rows sit in its LDS area (row r
     // of block b at b*16*K/32 + r*K/32); sc holds the lane's row's bytes of the current chunk.
     constexpr int SCB = SKC / 32;                       // scale bytes per row and chunk
-    uint8_t* sarea = reinterpret_cast<uint8_t*>(lds + SACT_ELEMS) + (threadIdx.x >> 6) * SCALE_WAVE_BYTES;
+    uint8_t* sarea = reinterpret_cast<uint8_t*>(lds + SACT_ELEMS) + (threadIdx.x >> 6) * scale_wave_bytes(SKMAX);
     uint32_t sc[2][4] = {};
     // the whole scale rows of the wave's blocks, once per tile: loaded into registers first
     // (their latency overlaps the first activation chunk's), then written to the LDS area
-    constexpr int SLD = WF == WF_BF16 ? 1 : SCALE_KMAX / 2 / 1024;   // 16-byte loads per lane and block
+    constexpr int SLD = WF == WF_BF16 ? 1 : (SKMAX / 2 + 1023) / 1024;   // 16-byte loads per lane and block
     u32x4 st[2][SLD];
     auto stage_s_load = [&]() {
         if constexpr (WF != WF_BF16) {
@@ -484,7 +485,7 @@ __host__ __device__ constexpr int stream_ring(int wf, int nrb) {
                          : STREAM_RING_BF16;
 }
 
-template <bool GATED, int WF, int NRB, int RING, int THREADS>
+template <bool GATED, int WF, int NRB, int RING, int THREADS, bool SMALL>
 __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
     const int lane = threadIdx.x & 63;
     f32x4 acc[NRB][2];
@@ -492,9 +493,12 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     for (int i = 0; i < NRB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the streaming loop takes tiles of up to 64 rows
     constexpr int CHUNK = stream_chunk(NRB);
-    if constexpr (NRB <= 4) {
+    if constexpr (SMALL) {
+        // the host checks K % 512 == 0 and K <= SCALE_KMAX_SMALL
+        tile_body_stream<GATED, WF, NRB, stream_ring(WF, NRB), THREADS, SCALE_KMAX_SMALL>(c, &lds[0][0], acc);
+    } else if constexpr (NRB <= 4) {
         if (c.K % CHUNK == 0 && (WF == WF_BF16 || c.K <= SCALE_KMAX))
-            tile_body_stream<GATED, WF, NRB, stream_ring(WF, NRB), THREADS>(c, &lds[0][0], acc);
+            tile_body_stream<GATED, WF, NRB, stream_ring(WF, NRB), THREADS, SCALE_KMAX>(c, &lds[0][0], acc);
         else
             tile_body<GATED, WF, NRB, RING, THREADS>(c, lds, acc);
     } else
@@ -520,16 +524,19 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS
     }
 }
 
-template <bool GATED, int WF, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// SMALL: every tile has at most 64 rows (at most 64 tokens, so no expert has more) and K is a
+// multiple of 512 and at most SCALE_KMAX_SMALL.  Only the stream variant is compiled, with
+// 52 KB of LDS and at most 168 registers, so that three work-groups fit on a compute unit.
+template <bool GATED, int WF, int WAVES, bool SMALL>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SMALL ? 3 : 2)))
 moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B1,
                      const uint8_t* __restrict__ S0, const uint8_t* __restrict__ S1, int K, int N, int top_k,
                      const int32_t* __restrict__ sorted_pairs, const TileEntry* __restrict__ tiles,
                      const int32_t* __restrict__ num_tiles, int n_col_blocks, uint16_t* __restrict__ C) {
     // the large-tile loop's buffers, or the streaming loop's activation chunks and the
     // waves' scale areas
-    constexpr int STREAM_ELEMS = SACT_ELEMS + WAVES * SCALE_WAVE_BYTES / 2;
-    constexpr int LDS_ELEMS = 2 * GROWS * GKS > STREAM_ELEMS ? 2 * GROWS * GKS : STREAM_ELEMS;
+    constexpr int STREAM_ELEMS = SACT_ELEMS + WAVES * scale_wave_bytes(SMALL ? SCALE_KMAX_SMALL : SCALE_KMAX) / 2;
+    constexpr int LDS_ELEMS = SMALL || STREAM_ELEMS > 2 * GROWS * GKS ? STREAM_ELEMS : 2 * GROWS * GKS;
     __shared__ __attribute__((aligned(16))) uint16_t lds_raw[LDS_ELEMS];
     auto lds = reinterpret_cast<uint16_t (*)[GROWS * GKS]>(lds_raw);
 
@@ -592,20 +599,30 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
     const int nrb = (te.row_count + 15) >> 4;
 
     constexpr int TH = WAVES * 64;
-    if (nrb > 16)
-        run_tile<GATED, WF, 18, 4, TH>(c, lds);
-    else if (nrb > 12)
-        run_tile<GATED, WF, 16, 4, TH>(c, lds);
-    else if (nrb > 8)
-        run_tile<GATED, WF, 12, 4, TH>(c, lds);
-    else if (nrb > 4)
-        run_tile<GATED, WF, 8, 4, TH>(c, lds);
-    else if (nrb > 2)
-        run_tile<GATED, WF, 4, 4, TH>(c, lds);
-    else if (nrb > 1)
-        run_tile<GATED, WF, 2, 4, TH>(c, lds);
-    else
-        run_tile<GATED, WF, 1, 4, TH>(c, lds);
+    if constexpr (SMALL) {
+        // at most 64 tokens: no expert has more than 64 rows
+        if (nrb > 2)
+            run_tile<GATED, WF, 4, 4, TH, true>(c, lds);
+        else if (nrb > 1)
+            run_tile<GATED, WF, 2, 4, TH, true>(c, lds);
+        else
+            run_tile<GATED, WF, 1, 4, TH, true>(c, lds);
+    } else {
+        if (nrb > 16)
+            run_tile<GATED, WF, 18, 4, TH, false>(c, lds);
+        else if (nrb > 12)
+            run_tile<GATED, WF, 16, 4, TH, false>(c, lds);
+        else if (nrb > 8)
+            run_tile<GATED, WF, 12, 4, TH, false>(c, lds);
+        else if (nrb > 4)
+            run_tile<GATED, WF, 8, 4, TH, false>(c, lds);
+        else if (nrb > 2)
+            run_tile<GATED, WF, 4, 4, TH, false>(c, lds);
+        else if (nrb > 1)
+            run_tile<GATED, WF, 2, 4, TH, false>(c, lds);
+        else
+            run_tile<GATED, WF, 1, 4, TH, false>(c, lds);
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1075,12 +1092,20 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4
 #endif
+// Work items whose weight rows hold at most this many bytes (10 whole-line steps: 4-bit
+// down at I = 2560) take the small-tile kernel at up to 64 tokens: three work-groups per
+// compute unit instead of two, so that more of each short item's start-up overlaps the
+// others' weight streams (4-bit down at 64 tokens 6% faster; 20-step items, 4-bit gate/up
+// and 8-bit down, 3% slower, 40- and 80-step items 3-4% slower).
+#ifndef SMALL_MAX_ROW_BYTES
+#define SMALL_MAX_ROW_BYTES 1280
+#endif
 
 template <bool GATED, int WF>
 static hipError_t launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, const uint8_t* B1, const uint8_t* S0,
-                        const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, const int32_t* sorted_pairs,
-                        const TileEntry* tiles, const int32_t* num_tiles, int64_t max_tile_count, uint16_t* C,
-                        hipStream_t s) {
+                        const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, int64_t max_rows,
+                        const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+                        int64_t max_tile_count, uint16_t* C, hipStream_t s) {
     constexpr int wide_min = WF == WF_BF16   ? WIDE_MIN_ROWS_PER_EXPERT
                              : WF == WF_E4M3 ? WIDE_MIN_ROWS_PER_EXPERT_E4M3
                                              : WIDE_MIN_ROWS_PER_EXPERT_E2M1;
@@ -1096,8 +1121,12 @@ static hipError_t launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t
         constexpr int W = DECODE_WAVES;
         const int ncb = N / (GATED ? W * 16 : W * 32);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
-        moe_gemm_bf16_kernel<GATED, WF, W><<<(unsigned)blocks, W * 64, 0, s>>>(
-            A, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
+        if (max_rows <= 64 && K % 512 == 0 && K <= SCALE_KMAX_SMALL && (int64_t)K * wbits(WF) / 8 <= SMALL_MAX_ROW_BYTES)
+            moe_gemm_bf16_kernel<GATED, WF, W, true><<<(unsigned)blocks, W * 64, 0, s>>>(
+                A, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
+        else
+            moe_gemm_bf16_kernel<GATED, WF, W, false><<<(unsigned)blocks, W * 64, 0, s>>>(
+                A, B0, B1, S0, S1, K, N, top_k, sorted_pairs, tiles, num_tiles, ncb, C);
     }
     return hipGetLastError();
 }
@@ -1113,17 +1142,17 @@ hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const 
     const uint64_t ab = (uint64_t)T * H * 2;
     const int64_t P = T * top_k;
     if (wf == WF_E4M3)
-        return launch_gemm<true, WF_E4M3>(A, ab, B0, B1, s_gate, s_up, H, I, top_k, P, E, sorted_pairs, tiles,
+        return launch_gemm<true, WF_E4M3>(A, ab, B0, B1, s_gate, s_up, H, I, top_k, P, E, T, sorted_pairs, tiles,
                                           num_tiles, max_tile_count, (uint16_t*)h, s);
     if (wf == WF_E2M1)
-        return launch_gemm<true, WF_E2M1>(A, ab, B0, B1, s_gate, s_up, H, I, top_k, P, E, sorted_pairs, tiles,
+        return launch_gemm<true, WF_E2M1>(A, ab, B0, B1, s_gate, s_up, H, I, top_k, P, E, T, sorted_pairs, tiles,
                                           num_tiles, max_tile_count, (uint16_t*)h, s);
-    return launch_gemm<true, WF_BF16>(A, ab, B0, B1, nullptr, nullptr, H, I, top_k, P, E, sorted_pairs, tiles,
+    return launch_gemm<true, WF_BF16>(A, ab, B0, B1, nullptr, nullptr, H, I, top_k, P, E, T, sorted_pairs, tiles,
                                       num_tiles, max_tile_count, (uint16_t*)h, s);
 }
 
-hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t P, int H,
-                       int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
+hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t T,
+                       int64_t P, int H, int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s) {
     if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
     if ((wf != WF_BF16) != (s_down != nullptr)) return hipErrorInvalidValue;
@@ -1131,12 +1160,12 @@ hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, con
     const uint8_t* B0 = (const uint8_t*)w_down;
     const uint64_t ab = (uint64_t)P * I * 2;
     if (wf == WF_E4M3)
-        return launch_gemm<false, WF_E4M3>(A, ab, B0, nullptr, s_down, nullptr, I, H, 0, P, E, sorted_pairs, tiles,
+        return launch_gemm<false, WF_E4M3>(A, ab, B0, nullptr, s_down, nullptr, I, H, 0, P, E, T, sorted_pairs, tiles,
                                            num_tiles, max_tile_count, (uint16_t*)y_pair, s);
     if (wf == WF_E2M1)
-        return launch_gemm<false, WF_E2M1>(A, ab, B0, nullptr, s_down, nullptr, I, H, 0, P, E, sorted_pairs, tiles,
+        return launch_gemm<false, WF_E2M1>(A, ab, B0, nullptr, s_down, nullptr, I, H, 0, P, E, T, sorted_pairs, tiles,
                                            num_tiles, max_tile_count, (uint16_t*)y_pair, s);
-    return launch_gemm<false, WF_BF16>(A, ab, B0, nullptr, nullptr, nullptr, I, H, 0, P, E, sorted_pairs, tiles,
+    return launch_gemm<false, WF_BF16>(A, ab, B0, nullptr, nullptr, nullptr, I, H, 0, P, E, T, sorted_pairs, tiles,
                                        num_tiles, max_tile_count, (uint16_t*)y_pair, s);
 }
 

@@ -199,6 +199,15 @@ MID_CASES = {
                                          weights="fp8", wr_std=math.sqrt(1.0 / 1024), seed_base=43000),
     "mid_mxfp4_items_e128_t96": mid_config("mid_mxfp4_items_e128_t96", 96, H=1024, I=1024, E=128, bias="zipf:0.12",
                                            weights="mxfp4", wr_std=math.sqrt(1.0 / 1024), seed_base=44000),
+    # at most 64 tokens with weight rows of at most 1280 bytes (8-bit and 4-bit at K = 1024):
+    # the decode kernel's small-tile variant (three work-groups per CU) for gate/up and down,
+    # the skew giving tiles of 1, 2 and up to 4 row blocks
+    "mid_fp8_skew_h1024_t64": mid_config("mid_fp8_skew_h1024_t64", 64, H=1024, I=1024, E=32, n_group=4,
+                                         topk_group=2, bias="zipf:0.6", weights="fp8",
+                                         wr_std=math.sqrt(1.0 / 1024), seed_base=48000),
+    "mid_mxfp4_skew_h1024_t64": mid_config("mid_mxfp4_skew_h1024_t64", 64, H=1024, I=1024, E=32, n_group=4,
+                                           topk_group=2, bias="zipf:0.6", weights="mxfp4",
+                                           wr_std=math.sqrt(1.0 / 1024), seed_base=49000),
     # the line kernel at K = 2560 (gate/up) and 1536 (down): 50 rows per expert, above every
     # format's switch (bf16 8, 8-bit 40, 4-bit 44), 12 and 10 column blocks, 40 and 24 steps
     "mid_line_h2560_t200": mid_config("mid_line_h2560_t200", 200, H=2560, I=1536, E=16, n_group=4, topk_group=2,
