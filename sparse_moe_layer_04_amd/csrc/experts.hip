@@ -458,7 +458,6 @@ __device__ __forceinline__ void tile_body_stream(const TileCtx& c, uint16_t* lds
     }
 }
 
-// Runs one tile: main loop variant, then the epilogue.
 // Register sets of the stream variant's weight ring (weights run ring-1 steps ahead),
 // measured over decode and serving shapes (16..1280 tokens of the Beam layer): bf16 two steps
 // ahead (three were 1% slower); E4M3 one step ahead in 16-row tiles and two in larger ones
@@ -485,6 +484,7 @@ __host__ __device__ constexpr int stream_ring(int wf, int nrb) {
                          : STREAM_RING_BF16;
 }
 
+// Runs one tile: main loop variant, then the epilogue.
 template <bool GATED, int WF, int NRB, int RING, int THREADS, bool SMALL>
 __device__ __forceinline__ void run_tile(const TileCtx& c, uint16_t (*lds)[GROWS * GKS]) {
     const int lane = threadIdx.x & 63;
