@@ -136,6 +136,10 @@ MID_CASES = {
     # 64-k stream (gate/up, K = 512) and 32-k steps (down, K = 256), and its large-tile loop
     "mid_fp8_prefill_t1000": mid_config("mid_fp8_prefill_t1000", 1000, weights="fp8", seed_base=21000),
     "mid_fp8_decode_t24": mid_config("mid_fp8_decode_t24", 24, weights="fp8", seed_base=22000),
+    # one token with quantized weights: eight tiles of one row (the small-tile decode kernel for
+    # gate/up at K = 512, 32-k steps for down at K = 256)
+    "mid_fp8_t1": mid_config("mid_fp8_t1", 1, weights="fp8", seed_base=50000),
+    "mid_mxfp4_t1": mid_config("mid_mxfp4_t1", 1, weights="mxfp4", seed_base=51000),
     "mid_fp8_skew_decode_t48": mid_config("mid_fp8_skew_decode_t48", 48, bias="zipf:0.6", weights="fp8",
                                           seed_base=23000),
     "mid_fp8_sublayer_t333": mid_config("mid_fp8_sublayer_t333", 333, sublayer=True, residual_k=40,
