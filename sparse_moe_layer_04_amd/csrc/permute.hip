@@ -35,6 +35,67 @@ __global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
+// Exclusive scans over experts of the row totals `tot` and the tile counts `ntl` (thread t
+// handles expert t; a 1024-thread work-group): inclusive scans inside each wave by shuffles,
+// then the totals of the earlier waves.  Writes off and toff, the row total to offsets[E] and
+// the tile total to *num_tiles.
+__device__ __forceinline__ void perm_expert_scan(int E, const int32_t* tot, const int32_t* ntl, int32_t* off,
+                                                 int32_t* toff, int32_t (*wsum)[16], int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ num_tiles) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t a = tid < E ? tot[tid] : 0, b = tid < E ? ntl[tid] : 0;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t ua = __shfl_up(a, o), ub = __shfl_up(b, o);
+        if (lane >= o) {
+            a += ua;
+            b += ub;
+        }
+    }
+    if (lane == 63) {
+        wsum[0][w] = a;
+        wsum[1][w] = b;
+    }
+    __syncthreads();
+    int32_t pa = 0, pb = 0;
+    for (int v = 0; v < w; ++v) {
+        pa += wsum[0][v];
+        pb += wsum[1][v];
+    }
+    if (tid < E) {
+        off[tid] = pa + a - tot[tid];
+        toff[tid] = pb + b - ntl[tid];
+    }
+    if (tid == 1023) {  // ids past E add zero
+        offsets[E] = pa + a;
+        if (num_tiles) *num_tiles = pb + b;
+    }
+}
+
+// Expert offsets and the balanced tile list (n = ceil(c / tile_rows) tiles per expert, the
+// rows split evenly).
+__device__ __forceinline__ void perm_write_tiles(int E, const int32_t* tot, const int32_t* ntl, const int32_t* off,
+                                                 const int32_t* toff, int32_t* __restrict__ offsets,
+                                                 TileEntry* __restrict__ tiles) {
+    for (int k = threadIdx.x; k < E; k += blockDim.x) {
+        offsets[k] = off[k];
+        if (tiles) {
+            const int n = ntl[k];
+            if (n > 0) {
+                const int c = tot[k];
+                const int r = (c + n - 1) / n;  // balanced rows per tile, <= tile_rows
+                for (int j = 0; j < n; ++j) {
+                    TileEntry te;
+                    te.expert = k;
+                    te.row_begin = off[k] + j * r;
+                    te.row_count = (c - j * r) < r ? (c - j * r) : r;
+                    te.group = n < 32768 ? (j << 16) | n : 0;
+                    tiles[toff[k] + j] = te;
+                }
+            }
+        }
+    }
+}
+
 // Scan by one work-group of 1024 threads.  Thread t handles expert t % E for chunk
 // group t / E (G = 1024 / E groups of consecutive chunks), so the per-expert scan over
 // chunks runs in G pieces with coalesced reads of the count rows; the scans over experts
@@ -78,37 +139,8 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
         ntl[tid] = run > 0 ? (run + tile_rows - 1) / tile_rows : 0;
     }
     __syncthreads();
-    // (3) exclusive scans over experts of the row counts and the tile counts: inclusive
-    // scans inside each wave by shuffles, then the totals of the earlier waves
-    {
-        const int lane = tid & 63, w = tid >> 6;
-        int32_t a = tid < E ? tot[tid] : 0, b = tid < E ? ntl[tid] : 0;
-        for (int o = 1; o < 64; o <<= 1) {
-            const int32_t ua = __shfl_up(a, o), ub = __shfl_up(b, o);
-            if (lane >= o) {
-                a += ua;
-                b += ub;
-            }
-        }
-        if (lane == 63) {
-            wsum[0][w] = a;
-            wsum[1][w] = b;
-        }
-        __syncthreads();
-        int32_t pa = 0, pb = 0;
-        for (int v = 0; v < w; ++v) {
-            pa += wsum[0][v];
-            pb += wsum[1][v];
-        }
-        if (tid < E) {
-            off[tid] = pa + a - tot[tid];
-            toff[tid] = pb + b - ntl[tid];
-        }
-        if (tid == 1023) {  // ids past E add zero
-            offsets[E] = pa + a;
-            if (num_tiles) *num_tiles = pb + b;
-        }
-    }
+    // (3) exclusive scans over experts of the row counts and the tile counts
+    perm_expert_scan(E, tot, ntl, off, toff, wsum, offsets, num_tiles);
     __syncthreads();
     // (4) every chunk's first row per expert: expert offset + earlier chunks' counts
     if (g < G) {
@@ -126,24 +158,7 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
         }
     }
     // (5) expert offsets and the balanced tile list
-    for (int k = tid; k < E; k += blockDim.x) {
-        offsets[k] = off[k];
-        if (tiles) {
-            const int n = ntl[k];
-            if (n > 0) {
-                const int c = tot[k];
-                const int r = (c + n - 1) / n;  // balanced rows per tile, <= tile_rows
-                for (int j = 0; j < n; ++j) {
-                    TileEntry te;
-                    te.expert = k;
-                    te.row_begin = off[k] + j * r;
-                    te.row_count = (c - j * r) < r ? (c - j * r) : r;
-                    te.group = n < 32768 ? (j << 16) | n : 0;
-                    tiles[toff[k] + j] = te;
-                }
-            }
-        }
-    }
+    perm_write_tiles(E, tot, ntl, off, toff, offsets, tiles);
 }
 
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ counts, int nchunks, int E,
@@ -223,14 +238,18 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
 // The histogram goes through `counts` (E words of the scratch) so the scan reads it as
 // in the multi-chunk path; wave 0 then places the pairs.
 __global__ void __launch_bounds__(1024) perm_single_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
-                                                           int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_pairs,
                                                            int32_t* __restrict__ pair_pos,
                                                            TileEntry* __restrict__ tiles,
                                                            int32_t* __restrict__ num_tiles, int tile_rows) {
+    // one chunk: the counts, the scans and the cursors stay in LDS
     __shared__ int32_t cnt[PERM_MAX_E];
+    __shared__ int32_t ntl[PERM_MAX_E];
+    __shared__ int32_t off[PERM_MAX_E];
+    __shared__ int32_t toff[PERM_MAX_E];
     __shared__ int32_t next[PERM_MAX_E];
+    __shared__ int32_t wsum[2][16];
     const int tid = threadIdx.x;
     int ev[PERM_SLICES];   // wave 0's ids for the scatter, in flight during the count and scan
     if (tid < 64) perm_load_ids(idx, 0, P, tid, ev);
@@ -241,11 +260,12 @@ __global__ void __launch_bounds__(1024) perm_single_kernel(const int32_t* __rest
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 1024) counts[e] = cnt[e];
+    if (tid < E) ntl[tid] = cnt[tid] > 0 ? (cnt[tid] + tile_rows - 1) / tile_rows : 0;
     __syncthreads();
-    perm_scan_body(counts, 1, E, offsets, tiles, num_tiles, tile_rows);
+    perm_expert_scan(E, cnt, ntl, off, toff, wsum, offsets, num_tiles);
     __syncthreads();
-    for (int e = tid; e < E; e += 1024) next[e] = counts[e];
+    if (tid < E) next[tid] = off[tid];
+    perm_write_tiles(E, cnt, ntl, off, toff, offsets, tiles);
     __syncthreads();
     const int ebits = perm_ebits(E);
 #pragma unroll
@@ -261,7 +281,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* scratch
                           int tile_rows, hipStream_t s) {
     int nchunks = (int)((P + PERM_CHUNK - 1) / PERM_CHUNK);
     if (nchunks == 1) {
-        perm_single_kernel<<<1, 1024, 0, s>>>(idx, P, E, scratch, offsets, sorted_pairs, pair_pos, tiles, num_tiles,
+        perm_single_kernel<<<1, 1024, 0, s>>>(idx, P, E, offsets, sorted_pairs, pair_pos, tiles, num_tiles,
                                               tile_rows);
         return hipGetLastError();
     }
