@@ -45,7 +45,6 @@ bool shape_supported(const beam_moe_shape* s) {
 struct Layout {
     size_t part = 0, idx = 0, w = 0, u = 0, scratch = 0, offsets = 0, sorted = 0, pos = 0, ntiles = 0, tiles = 0,
            h = 0, ypair = 0, total = 0;
-    int tile_rows = 0;
     int nsplit = 1;  // router reduction splits
     int64_t max_tiles = 0;
 };
@@ -67,8 +66,7 @@ Layout make_layout(const beam_moe_shape* s, int op) {
         L.scratch = take(beam::permute_scratch_words(P, s->E) * 4);
     } else {
         const bool bf16 = s->dtype == BEAM_BF16;
-        L.tile_rows = beam::gemm_tile_rows(P, s->E, bf16);
-        L.max_tiles = bf16 ? beam::max_tiles(P, s->E, L.tile_rows) : 0;
+        L.max_tiles = bf16 ? beam::max_tiles(P, s->E, beam::gemm_min_tile_rows()) : 0;
         L.part = take((size_t)L.nsplit * T * s->E * 8);
         L.idx = take((size_t)P * 4);
         L.w = take((size_t)P * 4);
@@ -219,6 +217,8 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     int32_t* sorted = at<int32_t>(ws, L.sorted);
     int32_t* ntiles = at<int32_t>(ws, L.ntiles);
     TileEntry* tiles = at<TileEntry>(ws, L.tiles);
+    const int wf = sc ? sc->format : beam::WF_BF16;
+    const int tile_rows = beam::gemm_tile_rows(P, E, H, I, bf16, wf);
 
     BEAM_TRY(mark(BEAM_STAGE_PRENORM));
     const void* act = x;
@@ -235,14 +235,14 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     BEAM_TRY(mark(BEAM_STAGE_PERMUTE));
     BEAM_TRY(beam::launch_permute(idx, P, E, at<int32_t>(ws, L.scratch), at<int32_t>(ws, L.offsets), sorted,
                                   at<int32_t>(ws, L.pos), bf16 ? tiles : nullptr, bf16 ? ntiles : nullptr,
-                                  L.tile_rows, s));
+                                  tile_rows, s));
     BEAM_TRY(mark(BEAM_STAGE_GATE_UP));
     void* h = at<void>(ws, L.h);
     void* ypair = at<void>(ws, L.ypair);
     if (bf16) {
-        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, sc ? sc->format : beam::WF_BF16,
+        BEAM_TRY(beam::launch_gate_up(act, true, w_gate, w_up, wf,
                                       sc ? sc->gate : nullptr, sc ? sc->up : nullptr, T, H, I, E, K, sorted, tiles,
-                                      ntiles, L.max_tiles, L.tile_rows, h, s));
+                                      ntiles, L.max_tiles, tile_rows, h, s));
     } else {
         BEAM_TRY(beam::launch_gate_up_f32(static_cast<const float*>(act), static_cast<const float*>(w_gate),
                                           static_cast<const float*>(w_up), H, I, K, sorted, idx, P,
@@ -250,8 +250,8 @@ beam_status forward_impl(const beam_moe_shape* shape, const void* x, const float
     }
     BEAM_TRY(mark(BEAM_STAGE_DOWN));
     if (bf16) {
-        BEAM_TRY(beam::launch_down(h, true, w_down, sc ? sc->format : beam::WF_BF16, sc ? sc->down : nullptr, T, P, H,
-                                   I, E, sorted, tiles, ntiles, L.max_tiles, L.tile_rows, ypair, s));
+        BEAM_TRY(beam::launch_down(h, true, w_down, wf, sc ? sc->down : nullptr, T, P, H,
+                                   I, E, sorted, tiles, ntiles, L.max_tiles, tile_rows, ypair, s));
     } else {
         BEAM_TRY(beam::launch_down_f32(static_cast<const float*>(h), static_cast<const float*>(w_down), H, I, sorted,
                                        idx, P, static_cast<float*>(ypair), s));

@@ -87,12 +87,15 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* scratch
 // upper bound on the number of tiles of at most `tile_rows` rows
 inline int64_t max_tiles(int64_t P, int E, int tile_rows) { return (P + tile_rows - 1) / tile_rows + E; }
 
-// rows per GEMM tile the forward pass uses for a given average load
-int gemm_tile_rows(int64_t P, int E, bool bf16);
-
 // expert weight storage: bf16, OCP FP8 E4M3 codes, or OCP FP4 E2M1 codes two per byte (the
 // last two with one E8M0 scale byte per 32 elements of a row along K)
 constexpr int WF_BF16 = 0, WF_E4M3 = 1, WF_E2M1 = 2;
+
+// rows per GEMM tile the forward pass uses for P pairs over E experts with weight format
+// wf (it depends on which GEMM kernel takes the batch), and the smallest it ever uses (the
+// workspace bounds the tile count with it)
+int gemm_tile_rows(int64_t P, int E, int H, int I, bool bf16, int wf);
+int gemm_min_tile_rows();
 // bits per stored weight
 __host__ __device__ constexpr int wbits(int wf) { return wf == WF_BF16 ? 16 : wf == WF_E4M3 ? 8 : 4; }
 

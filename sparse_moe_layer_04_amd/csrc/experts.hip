@@ -645,7 +645,18 @@ moe_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__
 // 32-bit offsets keep one address register per stream.
 // ---------------------------------------------------------------------------------
 constexpr int WKS = 64;                    // k per step
-constexpr int WBUF_ELEMS = GROWS * WKS;    // one LDS activation buffer (36 KB)
+// Rows per tile of the line kernel.  With 16- and 8-bit weights a tile holds up to 320 rows:
+// at 8192 tokens of the Beam layer every expert (at most ~313 rows there) then fits one tile,
+// so no expert's weights are streamed twice and the 256 x 20 work items of a GEMM fill the
+// 256 compute units in 20 whole rounds; with 288-row tiles nine experts split into two
+// half-full tiles and 5300 items leave the last round 70% full.  4-bit weights keep 288 rows:
+// their three-step register ring leaves no room for a 20th row block of accumulators.
+constexpr int LROWS = 320;
+template <int WF>
+__host__ __device__ constexpr int line_rows() { return WF == WF_E2M1 ? GROWS : LROWS; }
+// one LDS activation buffer (40 KB at 320 rows)
+template <int WF>
+constexpr int wbuf_elems() { return line_rows<WF>() * WKS; }
 constexpr int BUF_DWORD3 = 0x00020000;     // raw buffer descriptor word 3 on gfx9
 
 // LDS element offset of 16-byte chunk `ch` (0..7) of activation row `row` (128-byte
@@ -773,7 +784,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
     u32x4 sa[AL];
     auto kbytes = [&](int kstep) { return (uint32_t)((kstep < nk ? kstep : nk - 1) * WKS * 2); };
     auto load_a = [&](int i, int kstep) { sa[i] = buf_load(c.act, avoff[i], kbytes(kstep)); };
-    auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * WBUF_ELEMS + lds_slot(i)) = sa[i]; };
+    auto store_a = [&](int i, int buf) { *(u32x4*)(lds + buf * wbuf_elems<WF>() + lds_slot(i)) = sa[i]; };
     auto load_b = [&](int b, int kstep, int set) { line_load_b<NB, RING, WF>(c, rb, rs, wl, b, kstep, set); };
     // fragment read offsets: row r*16 + (lane & 15), LDS positions 2g and 2g+1 (g = lane >> 4).
     // bf16 weights: the even MFMA takes k-chunk g of the step's 128 bytes, the odd one k-chunk
@@ -811,7 +822,7 @@ __device__ __forceinline__ void line_body(const LineCtx& c, uint16_t* lds, u32x4
         constexpr int j = decltype(jc)::value;          // kt mod UNR
         constexpr int set = j % RING;
         constexpr int nset = (j + RING - 1) % RING;     // ring slot of step kt+RING-1
-        const uint16_t* L = lds + (j & 1) * WBUF_ELEMS;
+        const uint16_t* L = lds + (j & 1) * wbuf_elems<WF>();
         const int wbuf = (j + 1) & 1;
         if constexpr (WF == WF_BF16)
             lds_write_barrier();   // bf16 weights of the next step are loading into LDS
@@ -907,12 +918,15 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
     const int32_t* __restrict__ num_tiles, int n_col_blocks, uint16_t* __restrict__ C) {
     static_assert(WAVES * NB * 16 == 256 && NB % 2 == 0, "a work-group covers 256 weight rows");
     // the output tile is staged through LDS (rows padded by 16 bytes) once the main loop is
-    // done, EPI_RB row blocks at a time (bf16 down: half the tile, so that with the bf16
-    // weight slots below everything fits in 160 KB)
+    // done, EPI_RB row blocks at a time (down: half the tile with bf16 weights or 320-row
+    // tiles, so that with the bf16 weight slots below everything fits in 160 KB)
     constexpr int EPI_COLS = GATED ? WAVES * (NB / 2) * 16 : WAVES * NB * 16;
     constexpr int EPI_STRIDE = EPI_COLS + 8;
-    constexpr int EPI_RB = GATED || WF != WF_BF16 ? GROWS / 16 : GROWS / 32;
-    constexpr int LDS_ELEMS = EPI_RB * 16 * EPI_STRIDE > 2 * WBUF_ELEMS ? EPI_RB * 16 * EPI_STRIDE : 2 * WBUF_ELEMS;
+    constexpr int ROWS = line_rows<WF>();
+    constexpr int EPI_RB = GATED || (WF != WF_BF16 && ROWS == GROWS) ? ROWS / 16 : ROWS / 32;
+    constexpr int WBUF = wbuf_elems<WF>();
+    constexpr int LDS_ELEMS = EPI_RB * 16 * EPI_STRIDE > 2 * WBUF ? EPI_RB * 16 * EPI_STRIDE : 2 * WBUF;
+    static_assert(2 * (LDS_ELEMS + 2 * (WF == WF_BF16 ? WAVES * NB * 16 * WKS : 8)) <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
     // bf16 weights: two slots (steps of even and odd parity), each wave's 16*NB rows x 128
     // bytes; two arrays, so that a read of one slot waits only for the loads into that slot
@@ -1032,9 +1046,12 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_line_kernel(
             }
         });
     };
-    // row-block variants: 13..18 cover prefill-sized experts without padding blocks
+    // row-block variants: 13..18 (and 20 for 320-row tiles) cover prefill-sized experts
+    // with little padding
     const int nrb = (te.row_count + 15) >> 4;
-    if (nrb > 17)
+    if (ROWS > GROWS && nrb > 18)
+        run(std::integral_constant<int, ROWS / 16>());
+    else if (nrb > 17)
         run(std::integral_constant<int, 18>());
     else if (nrb > 16)
         run(std::integral_constant<int, 17>());
@@ -1067,11 +1084,6 @@ constexpr int LINE_RING = 2;
 #define LINE_RING_Q 3
 #endif
 
-int gemm_tile_rows(int64_t P, int E, bool bf16) {
-    (void)P;
-    (void)E;
-    return bf16 ? GROWS : (1 << 30);  // the fp32 path does not use tiles
-}
 
 // Average rows per expert from which the line-streaming kernel is used.  bf16: below it
 // the decode kernel (4-wave work-groups, two per CU) is 1-2% faster; above it the line
@@ -1101,15 +1113,29 @@ int gemm_tile_rows(int64_t P, int E, bool bf16) {
 #define SMALL_MAX_ROW_BYTES 1280
 #endif
 
+static bool use_line_kernel(int64_t P, int E, int K, int wf) {
+    const int wide_min = wf == WF_BF16 ? WIDE_MIN_ROWS_PER_EXPERT
+                         : wf == WF_E4M3 ? WIDE_MIN_ROWS_PER_EXPERT_E4M3
+                                         : WIDE_MIN_ROWS_PER_EXPERT_E2M1;
+    return P >= (int64_t)wide_min * E && K % (2 * WKS) == 0;
+}
+
+int gemm_tile_rows(int64_t P, int E, int H, int I, bool bf16, int wf) {
+    if (!bf16) return 1 << 30;  // the fp32 path does not use tiles
+    // the two GEMMs share one tile list: larger tiles only when the line kernel takes both
+    if (use_line_kernel(P, E, H, wf) && use_line_kernel(P, E, I, wf))
+        return wf == WF_E4M3 ? line_rows<WF_E4M3>() : wf == WF_E2M1 ? line_rows<WF_E2M1>() : line_rows<WF_BF16>();
+    return GROWS;
+}
+
+int gemm_min_tile_rows() { return GROWS; }
+
 template <bool GATED, int WF>
 static hipError_t launch_gemm(const uint16_t* A, uint64_t a_bytes, const uint8_t* B0, const uint8_t* B1, const uint8_t* S0,
                         const uint8_t* S1, int K, int N, int top_k, int64_t P, int E, int64_t max_rows,
                         const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                         int64_t max_tile_count, uint16_t* C, hipStream_t s) {
-    constexpr int wide_min = WF == WF_BF16   ? WIDE_MIN_ROWS_PER_EXPERT
-                             : WF == WF_E4M3 ? WIDE_MIN_ROWS_PER_EXPERT_E4M3
-                                             : WIDE_MIN_ROWS_PER_EXPERT_E2M1;
-    if (P >= (int64_t)wide_min * E && K % (2 * WKS) == 0) {
+    if (use_line_kernel(P, E, K, WF)) {
         const int ncb = N / (GATED ? LINE_WAVES * (LINE_NB / 2) * 16 : LINE_WAVES * LINE_NB * 16);
         const int64_t blocks = (max_tile_count * ncb + 7) / 8 * 8;
         moe_gemm_line_kernel<GATED, WF, LINE_WAVES, LINE_NB, WF == WF_E2M1 ? LINE_RING_Q : LINE_RING><<<(unsigned)blocks, LINE_WAVES * 64, 0, s>>>(
@@ -1135,7 +1161,8 @@ hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const 
                           const uint8_t* s_gate, const uint8_t* s_up, int64_t T, int H, int I, int E, int top_k,
                           const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                           int64_t max_tile_count, int tile_rows, void* h, hipStream_t s) {
-    if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
+    if (!bf16 || max_tile_count <= 0 || tile_rows != gemm_tile_rows(T * top_k, E, H, I, true, wf))
+        return hipErrorInvalidValue;
     if ((wf != WF_BF16) != (s_gate != nullptr)) return hipErrorInvalidValue;
     const uint16_t* A = (const uint16_t*)act;
     const uint8_t *B0 = (const uint8_t*)w_gate, *B1 = (const uint8_t*)w_up;
@@ -1154,7 +1181,8 @@ hipError_t launch_gate_up(const void* act, bool bf16, const void* w_gate, const 
 hipError_t launch_down(const void* h, bool bf16, const void* w_down, int wf, const uint8_t* s_down, int64_t T,
                        int64_t P, int H, int I, int E, const int32_t* sorted_pairs, const TileEntry* tiles, const int32_t* num_tiles,
                        int64_t max_tile_count, int tile_rows, void* y_pair, hipStream_t s) {
-    if (!bf16 || max_tile_count <= 0 || tile_rows != GROWS) return hipErrorInvalidValue;
+    if (!bf16 || max_tile_count <= 0 || tile_rows != gemm_tile_rows(P, E, H, I, true, wf))
+        return hipErrorInvalidValue;
     if ((wf != WF_BF16) != (s_down != nullptr)) return hipErrorInvalidValue;
     const uint16_t* A = (const uint16_t*)h;
     const uint8_t* B0 = (const uint8_t*)w_down;

@@ -123,7 +123,8 @@ MID_CASES = {
     "mid_t1": mid_config("mid_t1", 1, seed_base=13000),
     "mid_skew_t700": mid_config("mid_skew_t700", 700, bias="zipf:0.6", seed_base=14000),
     "mid_sublayer_t333": mid_config("mid_sublayer_t333", 333, bias="zero", sublayer=True, seed_base=15000),
-    "mid_dense_t2503": mid_config("mid_dense_t2503", 2503, seed_base=17000),  # ~313 rows per expert: split tiles;
+    "mid_dense_t2503": mid_config("mid_dense_t2503", 2503, seed_base=17000),  # ~313 rows per expert: 320-row tiles
+    # (20 row blocks) and split ones;
     # T >= 1024 and not a multiple of 4: the selection's last 4-token work-group is partial
     # the largest routing shape the ABI takes: E = 1024 experts in 64 groups, top-32
     "mid_maxshape_t200": mid_config("mid_maxshape_t200", 200, H=256, E=1024, I=128, n_group=64, topk_group=8,
@@ -135,6 +136,9 @@ MID_CASES = {
     # 8-bit expert weights (E4M3 + E8M0 block scales): the line kernel, the decode kernel's
     # 64-k stream (gate/up, K = 512) and 32-k steps (down, K = 256), and its large-tile loop
     "mid_fp8_prefill_t1000": mid_config("mid_fp8_prefill_t1000", 1000, weights="fp8", seed_base=21000),
+    # ~313 rows per expert with 8-bit weights: the line kernel's 320-row tiles (20 row blocks)
+    # and experts above 320 rows split in two
+    "mid_fp8_dense_t2503": mid_config("mid_fp8_dense_t2503", 2503, weights="fp8", seed_base=52000),
     "mid_fp8_decode_t24": mid_config("mid_fp8_decode_t24", 24, weights="fp8", seed_base=22000),
     # one token with quantized weights: eight tiles of one row (the small-tile decode kernel for
     # gate/up at K = 512, 32-k steps for down at K = 256)
