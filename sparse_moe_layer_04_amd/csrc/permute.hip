@@ -96,6 +96,49 @@ __device__ __forceinline__ void perm_write_tiles(int E, const int32_t* tot, cons
     }
 }
 
+// Order of the experts' tiles in the work list (thread t handles expert t).  The GEMM kernels
+// hand each of the 8 XCDs a contiguous eighth of the work items, so the list is dealt into 8
+// runs of equal cost: experts sorted by the 16-row blocks of their tiles, largest first
+// (stable by id; empty experts last), then dealt to the runs in snake order (0..7, 7..0, ...),
+// each run taking its experts in that sorted order so that every compute unit starts with
+// the largest items.  At 8192 tokens of the Beam layer (one tile per expert) each XCD gets
+// 32 experts of about the same total rows instead of 32 consecutive ones, whose totals
+// differed by up to 3%: on one MI355X gate/up took 3.15 instead of 3.26 ms, and the down GEMM
+// after it 1.88 instead of 1.85 in either order (the faster gate/up leaves the clock lower
+// when down starts), the layer 5.39 instead of 5.44 ms.  pos[t] is expert t's place in the
+// list; only the order of the tiles changes, each tile's rows and results stay the same.
+__device__ __forceinline__ void perm_deal_order(int E, const int32_t* tot, const int32_t* ntl, int32_t* key,
+                                                int32_t* pos) {
+    const int tid = threadIdx.x;
+    if (tid < E) {
+        const int n = ntl[tid];
+        int k = 0;
+        if (n > 0) {
+            const int blocks = ((tot[tid] + n - 1) / n + 15) >> 4;
+            k = 1 + (blocks < 62 ? blocks : 62);
+        }
+        key[tid] = k;
+    }
+    __syncthreads();
+    if (tid < E) {
+        const int k = key[tid];
+        int s = 0;  // rank in the sorted order
+        for (int v = 0; v < E; ++v) {
+            const int kv = key[v];
+            s += (kv > k) | ((kv == k) & (v < tid));
+        }
+        const int r = s >> 3, w = s & 7;
+        const int bin = (r & 1) ? 7 - w : w;
+        // experts in the runs before this one: every full round gives each run one, the last
+        // partial round (E % 8 experts) gives one to the first E % 8 runs of its direction
+        const int full = E >> 3, m = E & 7;
+        const bool fwd = (full & 1) == 0;
+        int before = bin * full;
+        for (int b = 0; b < bin; ++b) before += fwd ? (b < m) : (b >= 8 - m);
+        pos[tid] = before + r;
+    }
+}
+
 // Scan by one work-group of 1024 threads.  Thread t handles expert t % E for chunk
 // group t / E (G = 1024 / E groups of consecutive chunks), so the per-expert scan over
 // chunks runs in G pieces with coalesced reads of the count rows; the scans over experts
@@ -108,6 +151,8 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
     __shared__ int32_t off[PERM_MAX_E];
     __shared__ int32_t ntl[PERM_MAX_E];
     __shared__ int32_t toff[PERM_MAX_E];
+    __shared__ int32_t pos[PERM_MAX_E];
+    __shared__ int32_t ntl_pos[PERM_MAX_E];   // tile counts in work-list order, then their scan
     __shared__ int32_t wsum[2][16];
     const int tid = threadIdx.x;
     const int G = 1024 / E;  // >= 1 since E <= 1024
@@ -139,8 +184,15 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
         ntl[tid] = run > 0 ? (run + tile_rows - 1) / tile_rows : 0;
     }
     __syncthreads();
-    // (3) exclusive scans over experts of the row counts and the tile counts
-    perm_expert_scan(E, tot, ntl, off, toff, wsum, offsets, num_tiles);
+    // (3) the experts' order in the work list (toff is scratch here), then exclusive scans of
+    // the row counts over experts and of the tile counts in that order
+    perm_deal_order(E, tot, ntl, toff, pos);
+    __syncthreads();
+    if (tid < E) ntl_pos[pos[tid]] = ntl[tid];
+    __syncthreads();
+    perm_expert_scan(E, tot, ntl_pos, off, ntl_pos, wsum, offsets, num_tiles);
+    __syncthreads();
+    if (tid < E) toff[tid] = ntl_pos[pos[tid]];
     __syncthreads();
     // (4) every chunk's first row per expert: expert offset + earlier chunks' counts
     if (g < G) {
