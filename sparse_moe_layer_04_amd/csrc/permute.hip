@@ -108,7 +108,7 @@ __device__ __forceinline__ void perm_write_tiles(int E, const int32_t* tot, cons
 // when down starts), the layer 5.39 instead of 5.44 ms.  pos[t] is expert t's place in the
 // list; only the order of the tiles changes, each tile's rows and results stay the same.
 __device__ __forceinline__ void perm_deal_order(int E, const int32_t* tot, const int32_t* ntl, int32_t* key,
-                                                int32_t* pos) {
+                                                int32_t* pos) {   // key: 16-byte aligned, E rounded up to 16 words
     const int tid = threadIdx.x;
     if (tid < E) {
         const int n = ntl[tid];
@@ -119,13 +119,24 @@ __device__ __forceinline__ void perm_deal_order(int E, const int32_t* tot, const
         }
         key[tid] = k;
     }
+    const int E16 = (E + 15) & ~15;   // keys padded to 16 with -1 (below every expert's key)
+    if (tid >= E && tid < E16) key[tid] = -1;
     __syncthreads();
     if (tid < E) {
         const int k = key[tid];
-        int s = 0;  // rank in the sorted order
-        for (int v = 0; v < E; ++v) {
-            const int kv = key[v];
-            s += (kv > k) | ((kv == k) & (v < tid));
+        int s = 0;  // rank in the sorted order: larger keys, then equal keys of lower ids
+        for (int v0 = 0; v0 < E16; v0 += 16) {
+            int4 kv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) kv[q] = *(const int4*)(key + v0 + 4 * q);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int v = v0 + 4 * q;
+                s += (kv[q].x > k) | ((kv[q].x == k) & (v < tid));
+                s += (kv[q].y > k) | ((kv[q].y == k) & (v + 1 < tid));
+                s += (kv[q].z > k) | ((kv[q].z == k) & (v + 2 < tid));
+                s += (kv[q].w > k) | ((kv[q].w == k) & (v + 3 < tid));
+            }
         }
         const int r = s >> 3, w = s & 7;
         const int bin = (r & 1) ? 7 - w : w;
@@ -150,7 +161,7 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
     __shared__ int32_t tot[PERM_MAX_E];
     __shared__ int32_t off[PERM_MAX_E];
     __shared__ int32_t ntl[PERM_MAX_E];
-    __shared__ int32_t toff[PERM_MAX_E];
+    __shared__ __attribute__((aligned(16))) int32_t toff[PERM_MAX_E];   // also the sort keys (read 4 at a time)
     __shared__ int32_t pos[PERM_MAX_E];
     __shared__ int32_t ntl_pos[PERM_MAX_E];   // tile counts in work-list order, then their scan
     __shared__ int32_t wsum[2][16];
