@@ -96,50 +96,73 @@ __device__ __forceinline__ void perm_write_tiles(int E, const int32_t* tot, cons
     }
 }
 
+// Exclusive scan of v[0..n) into out (a 1024-thread work-group, n <= 1024; out may alias v).
+__device__ __forceinline__ void perm_scan_one(int n, const int32_t* v, int32_t* out, int32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int32_t own = tid < n ? v[tid] : 0;
+    int32_t a = own;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(a, o);
+        if (lane >= o) a += u;
+    }
+    if (lane == 63) wsum[w] = a;
+    __syncthreads();
+    int32_t pa = 0;
+    for (int q = 0; q < w; ++q) pa += wsum[q];
+    if (tid < n) out[tid] = pa + a - own;
+}
+
 // Order of the experts' tiles in the work list (thread t handles expert t).  The GEMM kernels
 // hand each of the 8 XCDs a contiguous eighth of the work items, so the list is dealt into 8
 // runs of equal cost: experts sorted by the 16-row blocks of their tiles, largest first
 // (stable by id; empty experts last), then dealt to the runs in snake order (0..7, 7..0, ...),
 // each run taking its experts in that sorted order so that every compute unit starts with
-// the largest items.  At 8192 tokens of the Beam layer (one tile per expert) each XCD gets
+// the largest items.  The sort is a stable counting sort: ballots rank each expert among the
+// experts of its wave with the same key, and one scan over the (key, wave) counts in key order
+// gives each its place (a loop comparing every expert with every other took 9 us of the scan
+// kernel at 256 experts).  At 8192 tokens of the Beam layer (one tile per expert) each XCD gets
 // 32 experts of about the same total rows instead of 32 consecutive ones, whose totals
 // differed by up to 3%: on one MI355X gate/up took 3.15 instead of 3.26 ms, and the down GEMM
 // after it 1.88 instead of 1.85 in either order (the faster gate/up leaves the clock lower
 // when down starts), the layer 5.39 instead of 5.44 ms.  pos[t] is expert t's place in the
 // list; only the order of the tiles changes, each tile's rows and results stay the same.
-__device__ __forceinline__ void perm_deal_order(int E, const int32_t* tot, const int32_t* ntl, int32_t* key,
-                                                int32_t* pos) {   // key: 16-byte aligned, E rounded up to 16 words
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void perm_deal_order(int E, const int32_t* tot, const int32_t* ntl, int32_t* table,
+                                                int32_t* pos, int32_t* wsum) {
+    // table: 1024 words of LDS, cell (63 - key) * 16 + wave: the experts of a wave with a key
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int k = -1;
     if (tid < E) {
         const int n = ntl[tid];
-        int k = 0;
+        k = 0;
         if (n > 0) {
             const int blocks = ((tot[tid] + n - 1) / n + 15) >> 4;
             k = 1 + (blocks < 62 ? blocks : 62);
         }
-        key[tid] = k;
     }
-    const int E16 = (E + 15) & ~15;   // keys padded to 16 with -1 (below every expert's key)
-    if (tid >= E && tid < E16) key[tid] = -1;
+    table[tid] = 0;
+    __syncthreads();
+    // per wave: each expert's rank among the wave's experts with its key (ballots over the
+    // keys present), and the count of each key
+    int rw = 0;
+    if (w * 64 < E) {   // uniform per wave
+        unsigned long long todo = __ballot(tid < E);
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const int kl = __shfl(k, leader);
+            const unsigned long long m = __ballot(k == kl);
+            if (k == kl) rw = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == leader) table[(63 - kl) * 16 + w] = __popcll(m);
+            todo &= ~m;
+        }
+    }
+    __syncthreads();
+    // cells in (key descending, wave ascending) order: the scan gives each cell its first rank
+    perm_scan_one(1024, table, table, wsum);
     __syncthreads();
     if (tid < E) {
-        const int k = key[tid];
-        int s = 0;  // rank in the sorted order: larger keys, then equal keys of lower ids
-        for (int v0 = 0; v0 < E16; v0 += 16) {
-            int4 kv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) kv[q] = *(const int4*)(key + v0 + 4 * q);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int v = v0 + 4 * q;
-                s += (kv[q].x > k) | ((kv[q].x == k) & (v < tid));
-                s += (kv[q].y > k) | ((kv[q].y == k) & (v + 1 < tid));
-                s += (kv[q].z > k) | ((kv[q].z == k) & (v + 2 < tid));
-                s += (kv[q].w > k) | ((kv[q].w == k) & (v + 3 < tid));
-            }
-        }
-        const int r = s >> 3, w = s & 7;
-        const int bin = (r & 1) ? 7 - w : w;
+        const int s = table[(63 - k) * 16 + w] + rw;   // rank: larger keys, then equal keys of lower ids
+        const int r = s >> 3, wb = s & 7;
+        const int bin = (r & 1) ? 7 - wb : wb;
         // experts in the runs before this one: every full round gives each run one, the last
         // partial round (E % 8 experts) gives one to the first E % 8 runs of its direction
         const int full = E >> 3, m = E & 7;
@@ -161,7 +184,7 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
     __shared__ int32_t tot[PERM_MAX_E];
     __shared__ int32_t off[PERM_MAX_E];
     __shared__ int32_t ntl[PERM_MAX_E];
-    __shared__ __attribute__((aligned(16))) int32_t toff[PERM_MAX_E];   // also the sort keys (read 4 at a time)
+    __shared__ int32_t toff[PERM_MAX_E];   // first the sort's (key, wave) table
     __shared__ int32_t pos[PERM_MAX_E];
     __shared__ int32_t ntl_pos[PERM_MAX_E];   // tile counts in work-list order, then their scan
     __shared__ int32_t wsum[2][16];
@@ -197,7 +220,7 @@ __device__ __forceinline__ void perm_scan_body(int32_t* __restrict__ counts, int
     __syncthreads();
     // (3) the experts' order in the work list (toff is scratch here), then exclusive scans of
     // the row counts over experts and of the tile counts in that order
-    perm_deal_order(E, tot, ntl, toff, pos);
+    perm_deal_order(E, tot, ntl, toff, pos, wsum[0]);
     __syncthreads();
     if (tid < E) ntl_pos[pos[tid]] = ntl[tid];
     __syncthreads();
