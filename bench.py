@@ -461,6 +461,14 @@ def main():
               "(no sharding, no collectives); --gpus %d is not supported" % max(args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
+    from synth.configs import CONFIGS as _CONFIGS
+    if _CONFIGS[args.workload].weights == "bf16" and args.secondary != "none":
+        for n in args.secondary.split(","):   # secondary workloads share the primary's bf16 weights
+            if n and (n not in _CONFIGS or _CONFIGS[n].weights != "bf16"):
+                print("--secondary takes bf16 workloads only (%s); the 8-bit and 4-bit layers run as "
+                      "--workload or in the default prefill run" % n, file=sys.stderr)
+                sys.exit(2)
+
     import torch
     if args.copy_calib:
         copy_calibration(args.copy_calib)

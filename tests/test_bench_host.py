@@ -23,6 +23,16 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert p.stdout == ""
 
 
+def test_quantized_secondary_workloads_are_refused_before_any_gpu_work():
+    # secondary workloads reuse the primary's bf16 weights: a quantized name would run the bf16
+    # layer under the quantized label, so it is refused up front
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--secondary", "skew_t6000,prefill_t8192_fp8"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "prefill_t8192_fp8" in p.stderr and "bf16 workloads only" in p.stderr
+    assert p.stdout == ""
+
+
 def test_roofline_picks_the_binding_resource():
     # 2.5 PFLOP and 8 GB in one second: the flops take 1 s at peak, the bytes 1 ms -> mfma
     r = bench.roofline(2.5e15, 8e9, 2.0)
