@@ -39,6 +39,8 @@ GEMM_SOURCES = [os.path.join(ROOT, "sparse_moe_layer_04_amd", "csrc", "experts.h
 EXPERTS_SRC = GEMM_SOURCES[0]
 # the workloads timed besides the primary one, in this order
 OTHER_WORKLOADS = ("tiny_f32", "decode_t64", "skew_t6000", "sublayer_t32768")
+# serving shapes timed in the default prefill run (bf16 weights, the decode workload's inputs)
+SERVING_SWEEP = (16, 256, 1024, 2048, 4096)
 CPU_SUBSET = 256            # seeded token subset of the oracle baseline for the large workloads
 CPU_ONE_THREAD_TOKENS = 8   # prefill tokens of the one-thread oracle figure
 
@@ -386,9 +388,9 @@ def cpu_baseline(primary, hw, others=(), one_thread=True, w_scales=None):
             "one_thread": one}
 
 
-def sweep(base, hw, dw, sizes, steps, warmup, md_path="", scales=None):
+def sweep_rows(base, hw, dw, sizes, steps, warmup, scales=None, emit=None):
     """The layer at several token counts with the decode workload's input distributions
-    (serving shapes between decode and prefill); one JSON line per size."""
+    (serving shapes between decode and prefill): one row per size."""
     rows = []
     for T in sizes:
         c = base.replace(name="serve_t%d" % T, T=T)
@@ -399,7 +401,15 @@ def sweep(base, hw, dw, sizes, steps, warmup, md_path="", scales=None):
                "experts_touched": s["experts"]["touched"], "rows_per_expert": T * c.top_k / c.E,
                "mfma_frac": s["layer"]["mfma_frac"], "hbm_frac": s["layer"]["hbm_frac"]}
         rows.append(row)
-        print(json.dumps(row), flush=True)
+        if emit:
+            emit(row)
+    return rows
+
+
+def sweep(base, hw, dw, sizes, steps, warmup, md_path="", scales=None):
+    """sweep_rows with one JSON line per size (and optionally a markdown table)."""
+    rows = sweep_rows(base, hw, dw, sizes, steps, warmup, scales=scales,
+                      emit=lambda row: print(json.dumps(row), flush=True))
     if md_path:
         with open(md_path, "w") as f:
             f.write("| T | rows/expert | experts touched | ms / layer | tokens/s | gate/up ms | down ms | "
@@ -433,6 +443,9 @@ def main():
     ap.add_argument("--secondary", default=",".join(OTHER_WORKLOADS),
                     help="comma-separated workloads timed in the same run besides the primary one, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-serving-sweep", action="store_true",
+                    help="skip the serving shapes (decode inputs at %s tokens) of the default prefill run"
+                         % ",".join(str(t) for t in SERVING_SWEEP))
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the decode and prefill layers with 8-bit and 4-bit expert weights")
     ap.add_argument("--sweep", default="", metavar="T1,T2,...",
@@ -542,6 +555,12 @@ def main():
             s2 = summarize(c2, r2)
             log("%s: %.3f ms/step" % (c2.name, s2["ms_per_step"]))
             line["workloads"][c2.name] = s2
+    if cfg.name == "prefill_t8192" and not args.no_serving_sweep:
+        line["serving_sweep"] = [
+            {k: row[k] for k in ("T", "rows_per_expert", "experts_touched", "ms_per_step", "tokens_per_s",
+                                 "gate_up_ms", "down_ms", "mfma_frac", "hbm_frac")}
+            for row in sweep_rows(CONFIGS["decode_t64"], hw, dw, SERVING_SWEEP, 10, 2,
+                                  emit=lambda row: log("serving T=%d: %.3f ms/step" % (row["T"], row["ms_per_step"])))]
     del dw
     torch.cuda.empty_cache()
     if not args.no_fp8 and args.workload == "prefill_t8192":
