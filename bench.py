@@ -8,12 +8,13 @@ tiny fp32 layer, the 64-token decode layer, the skewed 6000-token layer and the 
 sublayer), the decode and prefill layers with 8-bit and 4-bit expert weights, and the CPU
 oracle as a baseline.  Prints ONE JSON line.
 
-Timing: W untimed warm-up steps, then K bare forwards, each bracketed by events on the
-launch stream (``ms_per_step`` is their median; the bracket around all K gives the mean);
+Timing: W untimed warm-up steps (every other workload and serving shape also warms for
+at least 0.2 s of its own layers, so that it is timed at its own steady clocks), then K
+bare forwards, each bracketed by events on the launch stream (``ms_per_step`` is their median; the bracket around all K gives the mean);
 the per-stage times come from a separate pass whose forwards record events at every stage
 boundary on the same stream.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prefill_t8192]
+  python bench.py [--gpus 1] [--steps 20] [--warmup 20] [--workload prefill_t8192]
   python bench.py --sweep 16,64,256,1024 [--sweep-md table.md]   # serving shapes, one line per size
   python bench.py --copy-calib 1024      # plain 1 GiB device copy (HBM counter calibration)
   python bench.py --workload W --ingest-pmc FETCH.csv WRITE.csv CALIB_FETCH.csv CALIB_WRITE.csv 1024
@@ -39,6 +40,9 @@ GEMM_SOURCES = [os.path.join(ROOT, "sparse_moe_layer_04_amd", "csrc", "experts.h
 EXPERTS_SRC = GEMM_SOURCES[0]
 # the workloads timed besides the primary one, in this order
 OTHER_WORKLOADS = ("tiny_f32", "decode_t64", "skew_t6000", "sublayer_t32768")
+# every workload besides the primary one (which warms exactly --warmup layers) and every
+# serving shape also warms for at least this long on its own layers before it is timed
+SECONDARY_WARM_S = 0.2
 # serving shapes timed in the default prefill run (bf16 weights, the decode workload's inputs)
 SERVING_SWEEP = (16, 256, 1024, 2048, 4096)
 CPU_SUBSET = 256            # seeded token subset of the oracle baseline for the large workloads
@@ -222,7 +226,7 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_workload(cfg, hw, dw, steps, warmup, scales=None, stage_steps=None):
+def run_workload(cfg, hw, dw, steps, warmup, scales=None, stage_steps=None, min_warm_s=0.0):
     """Times workload `cfg` (weights hw on the host, dw on the device; quantized weights come
     with `scales` = (host scales, device scales)).
 
@@ -255,6 +259,14 @@ def run_workload(cfg, hw, dw, steps, warmup, scales=None, stage_steps=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # then warm for at least min_warm_s of this workload's own layers: after an idle gap (the
+    # weights being made and uploaded) the clocks ramp up over the first ~30 ms of load, which
+    # a few short decode layers do not cover
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < min_warm_s:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -394,7 +406,7 @@ def sweep_rows(base, hw, dw, sizes, steps, warmup, scales=None, emit=None):
     rows = []
     for T in sizes:
         c = base.replace(name="serve_t%d" % T, T=T)
-        r = run_workload(c, hw, dw, steps, warmup, scales=scales)
+        r = run_workload(c, hw, dw, steps, warmup, scales=scales, min_warm_s=SECONDARY_WARM_S)
         s = summarize(c, r)
         row = {"workload": c.name, "T": T, "tokens_per_s": s["tokens_per_s"], "ms_per_step": s["ms_per_step"],
                "gate_up_ms": s["stages_ms"]["gate_up"], "down_ms": s["stages_ms"]["down"],
@@ -436,7 +448,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_t8192",
                     choices=["prefill_t8192", "decode_t64", "skew_t6000", "sublayer_t32768", "decode_t64_fp8",
                              "prefill_t8192_fp8", "decode_t64_mxfp4", "prefill_t8192_mxfp4"])
@@ -548,10 +560,10 @@ def main():
                 hw2 = make_inputs(c2)
                 hw2 = (hw2.w_router, hw2.w_gate, hw2.w_up, hw2.w_down)
                 dw2 = tuple(_dev(a) for a in hw2)
-                r2 = run_workload(c2, hw2, dw2, args.steps, args.warmup)
+                r2 = run_workload(c2, hw2, dw2, args.steps, args.warmup, min_warm_s=SECONDARY_WARM_S)
                 del dw2
             else:
-                r2 = run_workload(c2, hw, dw, args.steps, args.warmup)
+                r2 = run_workload(c2, hw, dw, args.steps, args.warmup, min_warm_s=SECONDARY_WARM_S)
             s2 = summarize(c2, r2)
             log("%s: %.3f ms/step" % (c2.name, s2["ms_per_step"]))
             line["workloads"][c2.name] = s2
@@ -576,7 +588,7 @@ def main():
             line[key] = {}
             for name in names:
                 c8 = CONFIGS[name]
-                r8 = run_workload(c8, hq, dq, args.steps, args.warmup, scales=(hs, ds))
+                r8 = run_workload(c8, hq, dq, args.steps, args.warmup, scales=(hs, ds), min_warm_s=SECONDARY_WARM_S)
                 s8 = summarize(c8, r8)
                 log("%s %s: %.3f ms/step" % (fmt, name, s8["ms_per_step"]))
                 line[key][name] = s8
