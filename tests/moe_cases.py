@@ -136,6 +136,14 @@ MID_CASES = {
     # 8-bit expert weights (E4M3 + E8M0 block scales): the line kernel, the decode kernel's
     # 64-k stream (gate/up, K = 512) and 32-k steps (down, K = 256), and its large-tile loop
     "mid_fp8_prefill_t1000": mid_config("mid_fp8_prefill_t1000", 1000, weights="fp8", seed_base=21000),
+    # expert counts that are not a multiple of 8, with more than one chunk of pairs: the work
+    # list dealt to the 8 XCD runs ends in a partial round (60 experts: 7 full rounds, the
+    # last dealt backwards; 20 experts: 2 full rounds, the last dealt forwards); 27-60 rows
+    # per expert on the line kernel, and 47 rows per expert with 8-bit weights
+    "mid_e60_t400": mid_config("mid_e60_t400", 400, E=60, n_group=4, topk_group=2, top_k=4, seed_base=53000),
+    "mid_e20_t300": mid_config("mid_e20_t300", 300, E=20, n_group=4, topk_group=2, top_k=4, seed_base=54000),
+    "mid_fp8_e60_t700": mid_config("mid_fp8_e60_t700", 700, E=60, n_group=4, topk_group=2, top_k=4,
+                                   weights="fp8", seed_base=55000),
     # ~313 rows per expert with 8-bit weights: the line kernel's 320-row tiles (20 row blocks)
     # and experts above 320 rows split in two
     "mid_fp8_dense_t2503": mid_config("mid_fp8_dense_t2503", 2503, weights="fp8", seed_base=52000),
