@@ -444,6 +444,35 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
 
 
+def dense_gemm_calibration(spec, seconds=3.0):
+    """The dense bf16 GEMM rate the board sustains: torch.matmul (hipBLASLt) on contiguous
+    M x K and K x N bf16 operands, called back to back for `seconds` after one second of
+    warm-up; the median call gives the TFLOP/s.  A reference point for the expert GEMMs,
+    not part of the layer."""
+    import torch
+    m, n, k = (int(v) for v in spec.split(","))
+    a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    times = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for e0, e1 in evs:
+            e0.record()
+            torch.matmul(a, b, out=c)
+            e1.record()
+        torch.cuda.synchronize()
+        times += [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms = statistics.median(times)
+    print(json.dumps({"dense_gemm_bf16": [m, n, k], "calls": len(times), "ms_median": ms,
+                      "tflops": 2.0 * m * n * k / (ms * 1e-3) / 1e12}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +494,9 @@ def main():
                          "and print one JSON line per size instead of the benchmark line")
     ap.add_argument("--sweep-md", default="", metavar="PATH", help="also write the sweep as a markdown table")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB")
+    ap.add_argument("--dense-gemm-calib", default="", metavar="M,N,K",
+                    help="time a plain bf16 torch.matmul (hipBLASLt) of this shape back to back: the dense "
+                         "GEMM rate the board sustains, a reference for the expert GEMMs")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "SKIP"),
                     help="print the per-kernel duration table of a rocprofv3 kernel trace, leaving out the "
                          "first SKIP dispatches of each kernel (no GPU needed)")
@@ -497,6 +529,9 @@ def main():
     import torch
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+        return
+    if args.dense_gemm_calib:
+        dense_gemm_calibration(args.dense_gemm_calib)
         return
     import sparse_moe_layer_04_amd  # noqa: F401  (fails loudly without the HIP library)
     from synth.configs import CONFIGS, expert_weights, make_inputs
